@@ -1,0 +1,106 @@
+"""Pins of oracle.quant: per-head FP8, per-block INT8, V transpose/permute (CPU)."""
+import numpy as np
+import pytest
+
+import gen
+from oracle import brute
+from oracle.quant import (as_f32, quant_fp8_per_head, quant_int8_per_block, v_permute,
+                          v_unpermute, perm_pi, s_pad, fp8_descale)
+from oracle.numerics import e4m3fn_decode
+
+
+def _tiny(seed, lens, h, d, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    t = int(sum(lens))
+    x = (rng.standard_normal((t, h, d)) * 3).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    if dtype == "bf16":
+        return gen.bf16_bits(x), cu
+    return x.astype(np.float16), cu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fp8_per_head_vs_brute(dtype):
+    x, cu = _tiny(1, [3, 5, 1], 3, 8, dtype)
+    codes, ds = quant_fp8_per_head(x, dtype)
+    bc, bds = brute.quant_fp8_per_head(as_f32(x, dtype))
+    assert np.array_equal(ds.view(np.uint32), bds.view(np.uint32))
+    assert np.array_equal(codes, bc)
+
+
+def test_fp8_descale_is_amax_over_448_and_zero_head():
+    x, _ = _tiny(2, [4], 3, 8)
+    x[:, 1, :] = 0                       # bf16 +0 everywhere in head 1
+    codes, ds = quant_fp8_per_head(x, "bf16")
+    a = np.abs(as_f32(x, "bf16"))
+    for h in (0, 2):
+        assert ds[h] == np.float32(a[:, h].max()) / np.float32(448)
+        # the amax element encodes to the largest finite code
+        assert np.abs(e4m3fn_decode(codes[:, h])).max() == 448.0
+    assert ds[1] == 1.0 and not codes[:, 1].any()
+    # a supplied amax gives the same result as the reduction
+    c2, d2 = quant_fp8_per_head(x, "bf16", amax_in=a.max(axis=(0, 2)))
+    assert np.array_equal(c2, codes) and np.array_equal(d2, ds)
+    assert fp8_descale(np.array([0.0, 448.0]))[1] == 1.0
+
+
+def test_int8_per_block_vs_brute():
+    x, cu = _tiny(3, [5, 11, 0, 7], 2, 4, "fp16")
+    codes, sc = quant_int8_per_block(x, "fp16", cu, max_seqlen=11, block_tokens=4)
+    bc, bsc = brute.quant_int8_per_block(as_f32(x, "fp16"), cu, 4)
+    assert np.array_equal(codes, bc)
+    nblk = sc.shape[2]
+    assert nblk == 3
+    for b in range(4):
+        L = cu[b + 1] - cu[b]
+        for h in range(2):
+            for j in range(nblk):
+                if j * 4 < L:
+                    assert sc[b, h, j] == bsc[(b, h, j)]
+                else:
+                    assert sc[b, h, j] == 0.0
+
+
+def test_int8_blocks_restart_at_each_sequence():
+    # one large value at token 2 of sequence 1 must only inflate that
+    # sequence's block 0, whatever the global token index is
+    lens = [6, 6]
+    x = np.ones((12, 1, 2), np.float16)
+    x[6 + 2, 0, 0] = 100
+    cu = np.array([0, 6, 12], np.int32)
+    _, sc = quant_int8_per_block(x, "fp16", cu, 6, block_tokens=4)
+    assert sc[0, 0, 0] == np.float32(1) / np.float32(127)
+    assert sc[0, 0, 1] == np.float32(1) / np.float32(127)
+    assert sc[1, 0, 0] == np.float32(100) / np.float32(127)
+    assert sc[1, 0, 1] == np.float32(1) / np.float32(127)
+
+
+def test_pi_definition_and_bijection():
+    p = perm_pi(np.arange(32))
+    assert sorted(p.tolist()) == list(range(32))
+    # lane group g of an operand reads stored positions 8g..8g+7, which hold
+    # tokens 4g..4g+3 and 16+4g..16+4g+3
+    for g in range(4):
+        toks = [j for j in range(32) if 8 * g <= p[j] < 8 * g + 8]
+        assert sorted(toks) == [4 * g + r for r in range(4)] + [16 + 4 * g + r for r in range(4)]
+    assert p[0] == 0 and p[17] == 5 and p[4] == 8 and p[31] == 31 and p[16] == 4
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_v_permute_inverse_and_padding(fp8):
+    lens = [37, 64, 1]
+    x, cu = _tiny(4, lens, 2, 8, "bf16")
+    out, ds = v_permute(x, "bf16", cu, max(lens), fp8=fp8)
+    assert out.shape == (3, 2, 8, s_pad(64)) and s_pad(64) == 128
+    rec = v_unpermute(out, lens)
+    ref = quant_fp8_per_head(x, "bf16")[0] if fp8 else x
+    for b in range(3):
+        assert np.array_equal(rec[b], ref[cu[b]:cu[b + 1]])
+    # explicit placement: token 17 of sequence 0, head 1, channel 3
+    assert out[0, 1, 3, 5] == ref[17, 1, 3]
+    assert out[1, 0, 2, 32 + 8] == ref[37 + 32 + 4, 0, 2]
+    # padding is +0
+    pos_of = (np.arange(128) // 32) * 32 + perm_pi(np.arange(128) % 32)
+    for b, L in enumerate(lens):
+        pad = np.setdiff1d(np.arange(128), pos_of[:L])
+        assert not out[b][:, :, pad].any()
