@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized-attention path on one MI355X.
+
+Headline (``value``): the SageAttention-style varlen prefill workload --
+B=8, lengths U{512..4096} (seeded), causal, 32 q / 8 kv heads, D=128, fp16
+Q/K/V with 1% offset channels -- one step = per-block int8 quant of Q and K
++ transposed/permuted fp16 V + int8-QK / fp16-PV prefill, all inputs already
+in HBM.  value = algorithmic attention FLOP of the step / step time, in
+TFLOP/s (4 * D * H_q * sum over sequences of L(L+1)/2).
+
+Also reported (``extra``): the paged fp8 decode (GB/s of K/V bytes), the
+long fp8 prefill with RoPE + paged append (TFLOP/s), the sparse MLA decode
+(GB/s) when available, each timed on its own.
+
+``roofline``: the prefill kernel alone, timed with HIP events on the stream
+it is launched on, against the MFMA peak of its two contractions (int8 QK at
+5.0 POP/s, fp16 PV at 2.5 PFLOP/s: 2 / (1/5000 + 1/2500) = 3333 TFLOP/s for
+equal flop counts).  ``cpu_baseline``: the fp64 oracle on a bounded sample
+of the same workload, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOPS (% FP8 MFMA peak); decode HBM GB/s (% of peak)"
+PEAK_FP8 = 5000.0        # TFLOP/s dense
+PEAK_I8 = 5000.0         # TOP/s dense
+PEAK_F16 = 2500.0        # TFLOP/s dense
+PEAK_HBM = 8000.0        # GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(lens) -> int:
+    return int(sum(int(L) * (int(L) + 1) // 2 for L in lens))
+
+
+def time_events(fn, iters, flush=None):
+    """Per-call durations (ms) of fn() with events on the current stream."""
+    import torch
+    out = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e))
+    return out
+
+
+def make_flush():
+    """Writes a 1 GiB buffer: evicts L2 and the 256 MB Infinity Cache."""
+    import torch
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    return lambda: buf.fill_(1)
+
+
+def bench_config2(steps, warmup):
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import SagePrefill
+    from tests.parity import to_dev
+    x = gen.config2()
+    lens = x["seqlens"]
+    p = SagePrefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
+                    int(lens.max()), x["sm_scale"], causal=True)
+    flops = 4.0 * 128 * 32 * causal_pairs(lens)
+    for _ in range(warmup):
+        p.run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        p.run()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = s.elapsed_time(e) / steps
+    # the prefill kernel alone (one launch per call), same stream
+    kms = time_events(p.attend, max(steps, 10))
+    kavg = float(np.mean(kms))
+    qms = time_events(p.quantize, max(steps // 2, 5))
+    return {
+        "x": x, "lens": lens, "flops": flops, "ms_per_step": ms, "wall_s": wall,
+        "kernel_ms": kavg, "kernel_ms_min": float(np.min(kms)), "quant_ms": float(np.mean(qms)),
+    }
+
+
+def bench_config3(iters):
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import PagedDecode
+    from tests.parity import to_dev
+    x = gen.config3()
+    p = PagedDecode(to_dev(x["q"]), to_dev(x["k_cache"]), to_dev(x["v_cache"]), to_dev(x["k_scale"]),
+                    to_dev(x["v_scale"]), to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]),
+                    to_dev(x["kv_last_page_len"]), x["max_kv_len"], x["sm_scale"])
+    del x["k_cache"], x["v_cache"]
+    kv_bytes = float(np.sum(x["kv_lens"].astype(np.int64)) * 8 * 128 * 2)
+    other = 64 * 32 * 128 * 2 * 2 + x["kv_indices"].size * 4 + 65 * 4 * 2
+    for _ in range(3):
+        p.run()
+    ms = time_events(p.run, iters, make_flush())
+    med = float(np.median(ms))
+    gbs = (kv_bytes + other) / (med * 1e-3) / 1e9
+    return {"ms": med, "ms_min": float(np.min(ms)), "bytes": kv_bytes + other, "GB/s": gbs,
+            "pct_hbm": 100 * gbs / PEAK_HBM}
+
+
+def bench_config5(iters):
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import AppendRopeFp8Prefill
+    from tests.parity import to_dev
+    x = gen.config5()
+    ps = x["page_size"]
+    kc = torch.zeros((x["num_pages"], ps, 64, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    q0, k0 = to_dev(x["q"]), to_dev(x["k"])
+    p = AppendRopeFp8Prefill(q0.clone(), k0.clone(), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
+                             to_dev(x["kv_len_before"]), 32768, to_dev(x["rope_cos_sin"]), kc, vc,
+                             to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]), ps, x["sm_scale"])
+    p.run()
+    torch.cuda.synchronize()
+    flops = 4.0 * 128 * 64 * causal_pairs([32768])
+    kms = time_events(p.prefill.attend, iters)
+    # whole pipeline: the append rotates q/k in place, so restore them first (untimed)
+
+    def restore():
+        p.q.copy_(q0)
+        p.k.copy_(k0)
+    pipe = time_events(p.run, max(2, iters // 2), restore)
+    med = float(np.median(kms))
+    return {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
+            "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
+            "pipeline_ms": float(np.median(pipe)),
+            "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12}
+
+
+def bench_config4(iters):
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import SparseMlaDecode
+    from tests.parity import to_dev
+    x = gen.config4()
+    p = SparseMlaDecode(to_dev(x["q"]), to_dev(x["kv_cache"]), to_dev(x["block_table"]),
+                        to_dev(x["kv_lens"]), to_dev(x["sparse_indices"]), x["sm_scale"])
+    nbytes = 32 * 2048 * 656 + 32 * 128 * 576 * 2 + 32 * 128 * 512 * 2 + 32 * 2048 * 4 + 32 * 1024 * 4
+    flops = 32 * 128 * 2048 * 2.0 * (576 + 512)
+    p.run()
+    torch.cuda.synchronize()
+    ms = time_events(p.run, iters, make_flush())
+    med = float(np.median(ms))
+    gbs = nbytes / (med * 1e-3) / 1e9
+    return {"ms": med, "ms_min": float(np.min(ms)), "bytes": nbytes, "GB/s": gbs,
+            "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12}
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the config-2 workload: whole
+    heads of the first sequence, added until the time budget is spent."""
+    from oracle.attention import dequant_int8_per_block, prefill_varlen
+    from oracle.quant import quant_int8_per_block, as_f32
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    cu = x["cu_seqlens"]
+    L = int(cu[1])
+    one = np.array([0, L], np.int32)
+    t0 = time.perf_counter()
+    qc, qs = quant_int8_per_block(x["q"][:L], "fp16", one, L)
+    kc, ks = quant_int8_per_block(x["k"][:L], "fp16", one, L)
+    qd = dequant_int8_per_block(qc, qs, one)
+    kd = dequant_int8_per_block(kc, ks, one)
+    vd = as_f32(x["v"][:L], "fp16").astype(np.float64)
+    heads = 0
+    t_att = 0.0
+    while heads < 32 and t_att < budget_s:
+        ta = time.perf_counter()
+        prefill_varlen(qd[:, heads:heads + 1], kd[:, heads // 4:heads // 4 + 1],
+                       vd[:, heads // 4:heads // 4 + 1], one, one, x["sm_scale"], True, "fp16")
+        t_att += time.perf_counter() - ta
+        heads += 1
+    flops = 4.0 * 128 * heads * L * (L + 1) / 2
+    return {"value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"config-2 sequence 0 (L={L}), {heads} of 32 q heads, causal, fp64 numpy; "
+                      f"{t_att:.1f} s of attention (quantization {time.perf_counter() - t0 - t_att:.1f} s not counted)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extra", default="c3,c5,c4", help="comma list of extra workloads (c3,c4,c5) or ''")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    import paged_kv_amd
+    paged_kv_amd.lib()
+
+    log("[bench] config2 (headline)")
+    r2 = bench_config2(a.steps, a.warmup)
+    value = r2["flops"] / (r2["ms_per_step"] * 1e-3) / 1e12
+    k_tflops = r2["flops"] / (r2["kernel_ms"] * 1e-3) / 1e12
+    peak_mixed = 2.0 / (1.0 / PEAK_I8 + 1.0 / PEAK_F16)
+    extra = {"config2": {"step_ms": r2["ms_per_step"], "prefill_kernel_ms": r2["kernel_ms"],
+                         "prefill_kernel_ms_min": r2["kernel_ms_min"], "quant_ms": r2["quant_ms"],
+                         "prefill_kernel_TFLOPS": k_tflops, "pct_fp8_peak_step": 100 * value / PEAK_FP8,
+                         "pct_fp8_peak_kernel": 100 * k_tflops / PEAK_FP8}}
+    for name, fn, it in (("c3", bench_config3, 20), ("c5", bench_config5, 5), ("c4", bench_config4, 30)):
+        if name not in a.extra.split(","):
+            continue
+        log(f"[bench] {name}")
+        try:
+            extra[{"c3": "config3_decode", "c5": "config5_long_prefill", "c4": "config4_sparse_mla"}[name]] = fn(it)
+        except Exception as ex:  # report, keep the headline line
+            extra[name] = {"error": f"{type(ex).__name__}: {ex}"}
+        torch.cuda.empty_cache()
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(r2["x"])
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": r2["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8 QK / fp16 PV (fp32 accumulate)",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "sage_int8_varlen_prefill: B=8, lens U{512..4096} seed 1002, causal, "
+                               "Hq=32, Hkv=8, D=128, fp16 in/out; step = int8 quant Q,K + V permute + prefill",
+                   "tokens": int(np.sum(r2["lens"])), "lens": [int(v) for v in r2["lens"]],
+                   "step_flop": r2["flops"]},
+        "pct_fp8_peak": 100 * value / PEAK_FP8,
+        "roofline": {"bound": "mfma", "achieved": k_tflops, "peak": peak_mixed, "unit": "TFLOP/s",
+                     "frac": k_tflops / peak_mixed, "traffic": None,
+                     "kernel": "k_prefill<128, int8 QK, fp16 V>",
+                     "per_launch_flop": r2["flops"], "avg_launch_ms": r2["kernel_ms"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * attnq.h -- C ABI of the quantized flash-attention forward path for MI355X
+ * (gfx950).  Library: paged_kv_amd/libattnq.so.
+ *
+ * The path computes  O = softmax(scale * Dequant(Q) Dequant(K)^T + mask) Dequant(V)
+ * (the formula of the Ascend "KvQuantSparseFlashAttention" page, with
+ * Dequant(x, s) = x * s) over varlen batches, paged KV caches, fp8-e4m3 inputs
+ * with per-head descales, SageAttention-style per-block int8 Q/K and
+ * MLA-absorb sparse decode.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees, copies to the host or synchronizes: each call
+ *    only validates its host arguments and enqueues kernels on `stream`
+ *    (0 = the null stream), in order, asynchronously.
+ *  - Return value: ATTNQ_OK (0) or a negative attnq_status.  On a negative
+ *    status nothing was enqueued and attnq_last_error() (thread-local) holds
+ *    a message.
+ *  - Host arguments are checked; device-side contents (cu_seqlens, page
+ *    indices, ...) are preconditions.  Kernels clamp every index they read
+ *    from device memory to the buffer bounds given on the host, so a broken
+ *    precondition gives wrong values, never an out-of-bounds access.
+ *  - Pointers must be 16-byte aligned (4-byte for int32/fp32 arrays).
+ *  - Layouts are row-major, last index contiguous.  T = total tokens of a
+ *    varlen batch; cu_seqlens are int32 prefix sums [B+1], cu[0] = 0,
+ *    cu[B] = T (the FlashInfer qo_indptr / kv_indptr of a ragged batch).
+ *  - 16-bit float data is bf16 or fp16 as named by an attnq_dtype; fp8 is
+ *    OCP e4m3fn (bias 7, max 448, S.1111.111 = NaN).
+ */
+#ifndef ATTNQ_H
+#define ATTNQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTNQ_ABI_VERSION 1
+
+typedef enum {
+  ATTNQ_OK = 0,
+  ATTNQ_EINVAL = -1,       /* bad argument (null pointer, size, alignment) */
+  ATTNQ_EUNSUPPORTED = -2, /* valid but not implemented (head_dim, dtype mix) */
+  ATTNQ_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_size() */
+  ATTNQ_ELAUNCH = -4       /* the HIP runtime refused a launch */
+} attnq_status;
+
+typedef enum { ATTNQ_BF16 = 0, ATTNQ_FP16 = 1, ATTNQ_FP8E4M3 = 2, ATTNQ_INT8 = 3 } attnq_dtype;
+
+typedef enum {
+  ATTNQ_Q_FP8_PER_HEAD = 0,   /* fp8 e4m3fn codes, one fp32 descale per head */
+  ATTNQ_Q_INT8_PER_BLOCK = 1, /* int8 codes, one fp32 scale per (seq, head, 128-token block) */
+  ATTNQ_Q_NONE = 2            /* unquantized 16-bit data */
+} attnq_qmode;
+
+int attnq_abi_version(void);
+const char* attnq_last_error(void);
+
+/*
+ * attn_quant_qk -- the varlen "quant qk" step (PaddleNLP "Sage Attention
+ * Support Varlen"; aiter "[Triton] FP8 with FA v3 API": fp8 q/k with their
+ * descales).
+ *   x        [total_tokens, num_heads, head_dim], x_dtype BF16 or FP16.
+ *   codes    same shape, 1 byte per element: e4m3fn (FP8_PER_HEAD) or int8.
+ *   scales   FP8_PER_HEAD:   fp32 [num_heads], descale = amax/448 (amax over
+ *                            all rows and channels of the head; 1 if amax = 0).
+ *            INT8_PER_BLOCK: fp32 [batch, num_heads, ceil(max_seqlen/block_tokens)],
+ *                            scale = amax/127 over block j = rows
+ *                            [cu[b] + j*bt, min(cu[b] + (j+1)*bt, cu[b+1])) (1 if
+ *                            amax = 0; 0 for blocks past the sequence's end).
+ *   Codes: v = x / scale (IEEE fp32 division); fp8: NaN -> 0x7F, |v| clamped to
+ *   448, round to nearest even, sign kept; int8: rint(v) clamped to [-127, 127].
+ *   cu_seqlens: required for INT8_PER_BLOCK, ignored (may be NULL) for FP8.
+ *   amax_in: optional fp32 [num_heads] per-head amax of x (e.g. from
+ *   attn_append_kv_rope); FP8_PER_HEAD then skips its reduction pass.
+ *   block_tokens must be 128.  head_dim in {64, 128}.
+ */
+int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int batch,
+                  int max_seqlen, int total_tokens, int num_heads, int head_dim, int mode,
+                  int block_tokens, const float* amax_in, void* codes, float* scales,
+                  hipStream_t stream);
+
+/*
+ * attn_quant_v_permute -- the varlen "quant_transpose_permute v" step
+ * (PaddleNLP "Sage Attention Support Varlen").
+ *   v      [total_tokens, num_kv_heads, head_dim], BF16 or FP16.
+ *   v_out  [batch, num_kv_heads, head_dim, S_pad], S_pad = round_up(max_seqlen, 128):
+ *          v_out[b][h][d][32*G + pi(j)] = enc(v[cu[b] + 32*G + j][h][d]) for
+ *          tokens 32*G + j < L_b, all-zero bytes past L_b, with
+ *          pi(j) = 8*((j%16)/4) + 4*(j/16) + j%4 (the order in which the
+ *          prefill kernel's PV operand reads a 32-token group).
+ *   mode   FP8_PER_HEAD: enc = e4m3fn code as in attn_quant_qk, 1 byte/element,
+ *          v_scales fp32 [num_kv_heads] receives the descales;
+ *          NONE: enc = the unchanged 16-bit value, v_scales ignored.
+ *   amax_in optional, as in attn_quant_qk.
+ */
+int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, int batch,
+                         int max_seqlen, int total_tokens, int num_kv_heads, int head_dim,
+                         int mode, const float* amax_in, void* v_out, float* v_scales,
+                         hipStream_t stream);
+
+/*
+ * attn_append_kv_rope -- RoPE + write of the new K/V into a paged 16-bit
+ * cache (PaddleNLP "write kv cache BF16/FP16 with RoPE"; FlashInfer's paged
+ * layout and rope_theta).
+ *   q [total_tokens, num_q_heads, head_dim], k/v [total_tokens, num_kv_heads, head_dim],
+ *   all of `dtype` (BF16 or FP16).  q and k are rotated IN PLACE; v is read.
+ *   Token i of sequence b has position p = (kv_len_before ? kv_len_before[b] : 0) + i.
+ *   rope_cos_sin fp32 [max_pos, head_dim/2, 2] = (cos, sin) of p*theta^(-2i/D),
+ *   built by the caller.  Rotate-half: for i < D/2, in fp32 with each product
+ *   and sum rounded separately,
+ *     y[i] = x[i]*c - x[i+D/2]*s,   y[i+D/2] = x[i+D/2]*c + x[i]*s,
+ *   then rounded to `dtype` (nearest even).
+ *   k_cache / v_cache [num_pages, page_size, num_kv_heads, head_dim] (NHD):
+ *   position p of sequence b goes to page kv_indices[kv_indptr[b] + p/page_size],
+ *   slot p % page_size; rotated k and unrotated v are written, nothing else.
+ *   amax_q/amax_k/amax_v: optional fp32 [heads] outputs, max |value| per head
+ *   of the stored rotated q, rotated k and v (input for attn_quant_qk's amax_in).
+ *   Tokens whose position is >= max_pos, or whose page index is outside
+ *   [0, num_pages), are not written.
+ */
+int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                        const int32_t* kv_len_before, int batch, int total_tokens,
+                        int num_q_heads, int num_kv_heads, int head_dim,
+                        const float* rope_cos_sin, int max_pos, void* k_cache, void* v_cache,
+                        const int32_t* kv_indptr, const int32_t* kv_indices, int num_pages,
+                        int page_size, float* amax_q, float* amax_k, float* amax_v,
+                        hipStream_t stream);
+
+/*
+ * attn_prefill_varlen -- causal or full attention over a ragged batch
+ * (FlashInfer BatchPrefillWithRaggedKVCacheRun; aiter flash_attn_func with fp8
+ * q/k/v and descales; PaddleNLP Sage attention over a varlen batch).
+ *   q [total_q, num_q_heads, head_dim] and k [total_k, num_kv_heads, head_dim]:
+ *     qk_dtype FP8E4M3 with scale_mode FP8_PER_HEAD (q_scale [Hq], k_scale [Hkv]), or
+ *     qk_dtype INT8 with scale_mode INT8_PER_BLOCK (q_scale [B, Hq, ceil(max_seqlen_q/128)],
+ *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk).
+ *   v_perm: attn_quant_v_permute's output for the keys, [B, Hkv, D, round_up(max_seqlen_k,128)];
+ *     v_dtype FP8E4M3 (v_scale [Hkv]) or FP16 / BF16 (v_scale ignored).
+ *   logit(i, j) = sm_scale * Dequant(q_i) . Dequant(k_j); q head h reads kv head
+ *   h / (Hq/Hkv).  causal: key j visible to query i iff j <= i + L_k - L_q
+ *   (bottom-right aligned).
+ *   o [total_q, num_q_heads, head_dim], o_dtype BF16 or FP16.
+ *   lse optional fp32 [num_q_heads, total_q], natural log; rows with no visible
+ *   key get o = 0 and lse = -inf.
+ *   Supported: head_dim 64 or 128; (FP8, FP8 V) or (INT8, FP16/BF16 V).
+ */
+int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk_dtype,
+                        int v_dtype, const float* q_scale, const float* k_scale,
+                        const float* v_scale, int scale_mode, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int batch, int max_seqlen_q,
+                        int max_seqlen_k, int total_q, int total_k, int num_q_heads,
+                        int num_kv_heads, int head_dim, float sm_scale, int causal, void* o,
+                        int o_dtype, float* lse, hipStream_t stream);
+
+/*
+ * attn_decode_paged -- one query token per sequence against a paged fp8 cache,
+ * split over KV chunks and merged by log-sum-exp (FlashInfer
+ * BatchDecodeWithPagedKVCachePlan/Run; aiter's paged fp8 flash_attn_with_kvcache).
+ *   q bf16 [batch, num_q_heads, head_dim]; k_cache / v_cache fp8 e4m3fn
+ *   [num_pages, page_size, num_kv_heads, head_dim] (NHD); k_scale / v_scale fp32 [Hkv].
+ *   kv_indptr [batch+1], kv_indices [kv_indptr[batch]], kv_last_page_len [batch]:
+ *   kv_len[b] = (kv_indptr[b+1]-kv_indptr[b]-1)*page_size + kv_last_page_len[b]
+ *   (0 if the sequence has no page); token t lives in page
+ *   kv_indices[kv_indptr[b] + t/page_size], slot t % page_size.
+ *   max_kv_len: host upper bound of every kv_len (sizes the split).
+ *   workspace: caller-owned device scratch of at least
+ *   attn_decode_paged_workspace_size(...) bytes (partial O and lse).
+ *   o bf16 [batch, num_q_heads, head_dim]; lse optional fp32 [batch, num_q_heads].
+ *   Supported: head_dim 128, num_q_heads % num_kv_heads == 0, group <= 16,
+ *   page_size a multiple of 16 and <= 1024.
+ */
+size_t attn_decode_paged_workspace_size(int batch, int num_q_heads, int head_dim, int max_kv_len,
+                                        int page_size);
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
+                      int num_pages, int page_size, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_kv_len, float sm_scale, void* workspace,
+                      size_t workspace_bytes, void* o, float* lse, hipStream_t stream);
+
+/*
+ * attn_sparse_mla_decode -- MLA-absorb sparse attention over int8 cache rows
+ * with per-token tile-128 scales (Ascend "KvQuantSparseFlashAttention":
+ * attention_mode 2, quant_scale_repo_mode 1, tile_size 128, rope_head_dim 64,
+ * PA_BSND paging, sparse_block_size 1, sparse_mode 0).
+ *   q bf16 [batch, s_q, num_heads, 576] = [q_nope 512 | q_rope 64].
+ *   kv_cache uint8 [num_blocks, block_size, 1, 656]; each 656-byte row is
+ *     512 int8 nope codes | 64 bf16 rope values | 4 fp32 scales (scale t covers
+ *     nope channels [128t, 128t+128)).  K = [codes*scale | rope], V = codes*scale.
+ *   block_table int32 [batch, max_blocks_per_seq]: token i of sequence b is row
+ *     i % block_size of block block_table[b][i / block_size].
+ *   kv_lens int32 [batch]; sparse_indices int32 [batch, s_q, 1, topk]: an entry is
+ *     used iff 0 <= idx < kv_lens[b] (valid entries first, -1 padding after);
+ *     each used entry is one softmax term.
+ *   o bf16 [batch, s_q, num_heads, 512]; lse optional fp32 [batch, s_q, num_heads];
+ *   rows with no used entry get o = 0 and lse = -inf.
+ *   num_heads in {1,2,4,8,16,32,48,64,128}; block_size a multiple of 16, <= 1024;
+ *   topk > 0.  workspace >= attn_sparse_mla_decode_workspace_size(...).
+ */
+size_t attn_sparse_mla_decode_workspace_size(int batch, int s_q, int num_heads, int topk);
+int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* kv_lens,
+                           const int32_t* sparse_indices, int topk, int batch, int s_q,
+                           int num_heads, int num_blocks, int block_size, float sm_scale,
+                           void* workspace, size_t workspace_bytes, void* o, float* lse,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTNQ_H */

@@ -1,0 +1,340 @@
+// C ABI of libattnq: host-side validation, launch geometry and status codes.
+// No entry point allocates, frees, copies or synchronizes; each validates its
+// host arguments first and only then enqueues kernels on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attnq.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return ATTNQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p, a) \
+  do { \
+    REQUIRE((p) != nullptr, ATTNQ_EINVAL, "%s must not be NULL", #p); \
+    REQUIRE(aligned((p), (a)), ATTNQ_EINVAL, "%s must be %d-byte aligned", #p, (int)(a)); \
+  } while (0)
+
+#define REQUIRE_OPT_PTR(p, a) \
+  do { \
+    REQUIRE((p) == nullptr || aligned((p), (a)), ATTNQ_EINVAL, "%s must be %d-byte aligned", #p, (int)(a)); \
+  } while (0)
+
+#define LAUNCHED(x) \
+  do { \
+    if (!(x)) return fail(ATTNQ_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(hipGetLastError())); \
+  } while (0)
+
+const float LOG2E = 1.4426950408889634f;
+
+bool is16(int dt) { return dt == ATTNQ_BF16 || dt == ATTNQ_FP16; }
+int round_up(int x, int m) { return ((x + m - 1) / m) * m; }
+
+}  // namespace
+
+extern "C" {
+
+int attnq_abi_version(void) { return ATTNQ_ABI_VERSION; }
+
+const char* attnq_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------- attn_quant_qk
+int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int batch, int max_seqlen,
+                  int total_tokens, int num_heads, int head_dim, int mode, int block_tokens,
+                  const float* amax_in, void* codes, float* scales, hipStream_t stream) {
+  REQUIRE(is16(x_dtype), ATTNQ_EUNSUPPORTED, "x_dtype must be BF16 or FP16");
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_heads > 0 && num_heads <= 1024, ATTNQ_EINVAL, "num_heads must be in [1, 1024] (got %d)", num_heads);
+  REQUIRE(total_tokens >= 0, ATTNQ_EINVAL, "total_tokens must be >= 0");
+  REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_INT8_PER_BLOCK, ATTNQ_EINVAL,
+          "mode must be FP8_PER_HEAD or INT8_PER_BLOCK");
+  REQUIRE_PTR(scales, 4);
+  if (total_tokens > 0) {
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(codes, 16);
+  }
+  REQUIRE_OPT_PTR(amax_in, 4);
+  const bool bf = x_dtype == ATTNQ_BF16;
+  if (mode == ATTNQ_Q_FP8_PER_HEAD) {
+    if (!amax_in) {
+      LAUNCHED(attnq::launch_fill_u32(reinterpret_cast<uint32_t*>(scales), num_heads, 0u, stream));
+      LAUNCHED(attnq::launch_amax(x, total_tokens, num_heads, head_dim, bf,
+                                  reinterpret_cast<uint32_t*>(scales), stream));
+    }
+    LAUNCHED(attnq::launch_finalize_scale(amax_in, scales, num_heads, 448.0f, stream));
+    LAUNCHED(attnq::launch_quant_fp8(x, (long)total_tokens * num_heads * head_dim, num_heads, head_dim,
+                                     bf, scales, codes, stream));
+    return ok();
+  }
+  REQUIRE(block_tokens == 128, ATTNQ_EUNSUPPORTED, "block_tokens must be 128 (got %d)", block_tokens);
+  REQUIRE(batch >= 0, ATTNQ_EINVAL, "batch must be >= 0");
+  REQUIRE(max_seqlen >= 0, ATTNQ_EINVAL, "max_seqlen must be >= 0");
+  REQUIRE(amax_in == nullptr, ATTNQ_EINVAL, "amax_in applies to FP8_PER_HEAD only");
+  REQUIRE_PTR(cu_seqlens, 4);
+  const int nblk = (max_seqlen + block_tokens - 1) / block_tokens;
+  LAUNCHED(attnq::launch_quant_int8_block(x, cu_seqlens, batch, num_heads, head_dim, block_tokens, nblk,
+                                          bf, total_tokens, codes, scales, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_quant_v_permute
+int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, int batch,
+                         int max_seqlen, int total_tokens, int num_kv_heads, int head_dim,
+                         int mode, const float* amax_in, void* v_out, float* v_scales,
+                         hipStream_t stream) {
+  REQUIRE(is16(v_dtype), ATTNQ_EUNSUPPORTED, "v_dtype must be BF16 or FP16");
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_kv_heads > 0 && num_kv_heads <= 1024, ATTNQ_EINVAL, "num_kv_heads must be in [1, 1024]");
+  REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0, ATTNQ_EINVAL, "sizes must be >= 0");
+  REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_NONE, ATTNQ_EINVAL,
+          "mode must be FP8_PER_HEAD or NONE");
+  REQUIRE_PTR(cu_seqlens, 4);
+  REQUIRE_OPT_PTR(amax_in, 4);
+  const int s_pad = round_up(max_seqlen, 128);
+  if (batch > 0 && s_pad > 0) REQUIRE_PTR(v_out, 16);
+  if (total_tokens > 0) REQUIRE_PTR(v, 16);
+  const bool bf = v_dtype == ATTNQ_BF16;
+  const bool fp8 = mode == ATTNQ_Q_FP8_PER_HEAD;
+  if (fp8) {
+    REQUIRE_PTR(v_scales, 4);
+    if (!amax_in) {
+      LAUNCHED(attnq::launch_fill_u32(reinterpret_cast<uint32_t*>(v_scales), num_kv_heads, 0u, stream));
+      LAUNCHED(attnq::launch_amax(v, total_tokens, num_kv_heads, head_dim, bf,
+                                  reinterpret_cast<uint32_t*>(v_scales), stream));
+    }
+    LAUNCHED(attnq::launch_finalize_scale(amax_in, v_scales, num_kv_heads, 448.0f, stream));
+  }
+  LAUNCHED(attnq::launch_v_permute(v, cu_seqlens, batch, num_kv_heads, head_dim, s_pad, bf,
+                                   total_tokens, fp8, fp8 ? v_scales : nullptr, v_out, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_append_kv_rope
+int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                        const int32_t* kv_len_before, int batch, int total_tokens,
+                        int num_q_heads, int num_kv_heads, int head_dim,
+                        const float* rope_cos_sin, int max_pos, void* k_cache, void* v_cache,
+                        const int32_t* kv_indptr, const int32_t* kv_indices, int num_pages,
+                        int page_size, float* amax_q, float* amax_k, float* amax_v,
+                        hipStream_t stream) {
+  REQUIRE(is16(dtype), ATTNQ_EUNSUPPORTED, "dtype must be BF16 or FP16");
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_q_heads > 0 && num_kv_heads > 0, ATTNQ_EINVAL, "head counts must be positive");
+  REQUIRE(attnq::rope_units_fit(num_q_heads, num_kv_heads, head_dim), ATTNQ_EUNSUPPORTED,
+          "num_q_heads + 2*num_kv_heads too large for one token per workgroup");
+  REQUIRE(batch >= 1 && total_tokens >= 0, ATTNQ_EINVAL, "batch must be >= 1, total_tokens >= 0");
+  REQUIRE(page_size > 0 && page_size <= 1024, ATTNQ_EINVAL, "page_size must be in [1, 1024]");
+  REQUIRE(num_pages > 0 && max_pos > 0, ATTNQ_EINVAL, "num_pages and max_pos must be positive");
+  REQUIRE_PTR(cu_seqlens, 4);
+  REQUIRE_PTR(kv_indptr, 4);
+  REQUIRE_PTR(kv_indices, 4);
+  REQUIRE_PTR(rope_cos_sin, 16);
+  REQUIRE_PTR(k_cache, 16);
+  REQUIRE_PTR(v_cache, 16);
+  REQUIRE_OPT_PTR(kv_len_before, 4);
+  REQUIRE_OPT_PTR(amax_q, 4);
+  REQUIRE_OPT_PTR(amax_k, 4);
+  REQUIRE_OPT_PTR(amax_v, 4);
+  if (total_tokens > 0) {
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(k, 16);
+    REQUIRE_PTR(v, 16);
+  }
+  if (amax_q) LAUNCHED(attnq::launch_fill_u32(reinterpret_cast<uint32_t*>(amax_q), num_q_heads, 0u, stream));
+  if (amax_k) LAUNCHED(attnq::launch_fill_u32(reinterpret_cast<uint32_t*>(amax_k), num_kv_heads, 0u, stream));
+  if (amax_v) LAUNCHED(attnq::launch_fill_u32(reinterpret_cast<uint32_t*>(amax_v), num_kv_heads, 0u, stream));
+  LAUNCHED(attnq::launch_append_rope(q, k, v, dtype == ATTNQ_BF16, cu_seqlens, kv_len_before, batch,
+                                     total_tokens, num_q_heads, num_kv_heads, head_dim, rope_cos_sin,
+                                     max_pos, k_cache, v_cache, kv_indptr, kv_indices, num_pages,
+                                     page_size, amax_q, amax_k, amax_v, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_prefill_varlen
+int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk_dtype,
+                        int v_dtype, const float* q_scale, const float* k_scale,
+                        const float* v_scale, int scale_mode, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int batch, int max_seqlen_q,
+                        int max_seqlen_k, int total_q, int total_k, int num_q_heads,
+                        int num_kv_heads, int head_dim, float sm_scale, int causal, void* o,
+                        int o_dtype, float* lse, hipStream_t stream) {
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0, ATTNQ_EINVAL,
+          "num_q_heads must be a positive multiple of num_kv_heads");
+  const bool fp8qk = qk_dtype == ATTNQ_FP8E4M3 && scale_mode == ATTNQ_Q_FP8_PER_HEAD;
+  const bool i8qk = qk_dtype == ATTNQ_INT8 && scale_mode == ATTNQ_Q_INT8_PER_BLOCK;
+  REQUIRE(fp8qk || i8qk, ATTNQ_EUNSUPPORTED,
+          "supported Q/K: FP8E4M3 with FP8_PER_HEAD scales or INT8 with INT8_PER_BLOCK scales");
+  REQUIRE(v_dtype == ATTNQ_FP8E4M3 || v_dtype == ATTNQ_FP16, ATTNQ_EUNSUPPORTED, "v_dtype must be FP8E4M3 or FP16");
+  REQUIRE(is16(o_dtype), ATTNQ_EUNSUPPORTED, "o_dtype must be BF16 or FP16");
+  REQUIRE(batch >= 0 && max_seqlen_q >= 0 && max_seqlen_k >= 0 && total_q >= 0 && total_k >= 0,
+          ATTNQ_EINVAL, "sizes must be >= 0");
+  REQUIRE(max_seqlen_q <= 65535 * 128, ATTNQ_EINVAL, "max_seqlen_q too large");
+  REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
+  REQUIRE_PTR(cu_seqlens_q, 4);
+  REQUIRE_PTR(cu_seqlens_k, 4);
+  REQUIRE_PTR(q_scale, 4);
+  REQUIRE_PTR(k_scale, 4);
+  if (v_dtype == ATTNQ_FP8E4M3) REQUIRE_PTR(v_scale, 4);
+  if (total_q > 0) {
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(o, 16);
+  }
+  if (total_k > 0) {
+    REQUIRE_PTR(k, 16);
+    REQUIRE_PTR(v_perm, 16);
+  }
+  REQUIRE_OPT_PTR(lse, 4);
+  attnq::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v_perm;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.o = o; a.lse = lse;
+  a.batch = batch; a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.s_pad = round_up(max_seqlen_k, 128);
+  a.nblk_q = (max_seqlen_q + 127) / 128;
+  a.nblk_k = (max_seqlen_k + 127) / 128;
+  a.total_q = total_q; a.total_k = total_k;
+  a.causal = causal ? 1 : 0;
+  a.max_q = max_seqlen_q;
+  a.max_k = max_seqlen_k;
+  a.sm_scale_log2 = sm_scale * LOG2E;
+  if (total_q == 0) return ok();
+  LAUNCHED(attnq::launch_prefill(a, head_dim, i8qk, v_dtype == ATTNQ_FP8E4M3, o_dtype == ATTNQ_BF16,
+                                 max_seqlen_q, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_decode_paged
+size_t attn_decode_paged_workspace_size(int batch, int num_q_heads, int head_dim, int max_kv_len,
+                                        int page_size) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_kv_len < 0) return 0;
+  return attnq::decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len, page_size);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
+                      int num_pages, int page_size, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_kv_len, float sm_scale, void* workspace,
+                      size_t workspace_bytes, void* o, float* lse, hipStream_t stream) {
+  REQUIRE(head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0, ATTNQ_EINVAL,
+          "num_q_heads must be a positive multiple of num_kv_heads");
+  REQUIRE(num_q_heads / num_kv_heads <= 16, ATTNQ_EUNSUPPORTED, "at most 16 q heads per kv head");
+  REQUIRE(page_size >= 16 && page_size <= 1024 && page_size % 16 == 0, ATTNQ_EINVAL,
+          "page_size must be a multiple of 16 in [16, 1024] (got %d)", page_size);
+  REQUIRE(batch >= 0 && max_kv_len >= 0, ATTNQ_EINVAL, "batch and max_kv_len must be >= 0");
+  REQUIRE(num_pages > 0, ATTNQ_EINVAL, "num_pages must be positive");
+  REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
+  if (batch == 0) return ok();
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(k_cache, 16);
+  REQUIRE_PTR(v_cache, 16);
+  REQUIRE_PTR(k_scale, 4);
+  REQUIRE_PTR(v_scale, 4);
+  REQUIRE_PTR(kv_indptr, 4);
+  REQUIRE_PTR(kv_indices, 4);
+  REQUIRE_PTR(kv_last_page_len, 4);
+  REQUIRE_PTR(o, 16);
+  REQUIRE_OPT_PTR(lse, 4);
+  REQUIRE_PTR(workspace, 256);
+  const size_t need = attn_decode_paged_workspace_size(batch, num_q_heads, head_dim, max_kv_len, page_size);
+  REQUIRE(workspace_bytes >= need, ATTNQ_EWORKSPACE, "workspace too small: %zu < %zu bytes",
+          workspace_bytes, need);
+  attnq::DecodeArgs a;
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.k_scale = k_scale; a.v_scale = v_scale;
+  a.kv_indptr = kv_indptr; a.kv_indices = kv_indices; a.kv_last = kv_last_page_len;
+  a.o = o; a.lse = lse;
+  a.batch = batch; a.num_pages = num_pages; a.page_size = page_size;
+  a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.n_chunks = attnq::decode_n_chunks(max_kv_len);
+  a.chunk_pages = attnq::decode_chunk_pages(page_size);
+  const size_t rows = (size_t)batch * num_q_heads * a.n_chunks;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + rows * head_dim;
+  a.sm_scale_log2 = sm_scale * LOG2E;
+  LAUNCHED(attnq::launch_decode(a, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_sparse_mla_decode
+size_t attn_sparse_mla_decode_workspace_size(int batch, int s_q, int num_heads, int topk) {
+  if (batch <= 0 || s_q <= 0 || num_heads <= 0 || topk <= 0) return 0;
+  return attnq::mla_workspace_bytes(batch, s_q, num_heads, topk);
+}
+
+int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* kv_lens,
+                           const int32_t* sparse_indices, int topk, int batch, int s_q,
+                           int num_heads, int num_blocks, int block_size, float sm_scale,
+                           void* workspace, size_t workspace_bytes, void* o, float* lse,
+                           hipStream_t stream) {
+  static const int kHeads[] = {1, 2, 4, 8, 16, 32, 48, 64, 128};
+  bool heads_ok = false;
+  for (int h : kHeads) heads_ok |= (h == num_heads);
+  REQUIRE(heads_ok, ATTNQ_EUNSUPPORTED, "num_heads must be one of 1,2,4,8,16,32,48,64,128 (got %d)", num_heads);
+  REQUIRE(topk > 0, ATTNQ_EINVAL, "topk must be > 0 (got %d)", topk);
+  REQUIRE(block_size >= 16 && block_size <= 1024 && block_size % 16 == 0, ATTNQ_EINVAL,
+          "block_size must be a multiple of 16 in [16, 1024] (got %d)", block_size);
+  REQUIRE(batch >= 0 && s_q >= 0, ATTNQ_EINVAL, "batch and s_q must be >= 0");
+  REQUIRE(num_blocks > 0 && max_blocks_per_seq > 0, ATTNQ_EINVAL, "num_blocks and max_blocks_per_seq must be positive");
+  REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
+  if (batch == 0 || s_q == 0) return ok();
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(kv_cache, 16);
+  REQUIRE_PTR(block_table, 4);
+  REQUIRE_PTR(kv_lens, 4);
+  REQUIRE_PTR(sparse_indices, 4);
+  REQUIRE_PTR(o, 16);
+  REQUIRE_OPT_PTR(lse, 4);
+  REQUIRE_PTR(workspace, 256);
+  const size_t need = attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk);
+  REQUIRE(workspace_bytes >= need, ATTNQ_EWORKSPACE, "workspace too small: %zu < %zu bytes",
+          workspace_bytes, need);
+  attnq::MlaArgs a;
+  a.q = q;
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table; a.kv_lens = kv_lens; a.idx = sparse_indices;
+  a.o = o; a.lse = lse;
+  a.batch = batch; a.s_q = s_q; a.heads = num_heads; a.num_blocks = num_blocks;
+  a.block_size = block_size; a.max_blocks = max_blocks_per_seq; a.topk = topk;
+  a.n_split = attnq::mla_n_split(topk);
+  const size_t rows = (size_t)batch * s_q * a.n_split * num_heads;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + rows * 512;
+  a.sm_scale_log2 = sm_scale * LOG2E;
+  LAUNCHED(attnq::launch_mla(a, stream));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the HIP kernels of libattnq (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define ATTNQ_DEV __device__ __forceinline__
+
+namespace attnq {
+
+// ---------------------------------------------------------------- 16-bit floats
+ATTNQ_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+ATTNQ_DEV uint32_t f32_to_bf16(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+ATTNQ_DEV float f16_to_f32(uint32_t bits16) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return (float)h;
+}
+
+ATTNQ_DEV uint32_t f32_to_f16(float f) {  // hardware conversion, round to nearest even
+  _Float16 h = (_Float16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// 16-bit storage value -> fp32, `is_bf16` selects the format.
+ATTNQ_DEV float h16_to_f32(uint32_t bits16, bool is_bf16) {
+  return is_bf16 ? bf16_to_f32(bits16) : f16_to_f32(bits16);
+}
+ATTNQ_DEV uint32_t f32_to_h16(float f, bool is_bf16) {
+  return is_bf16 ? f32_to_bf16(f) : f32_to_f16(f);
+}
+
+// ---------------------------------------------------------------- fp8 e4m3fn
+// Encode v (already divided by its scale): NaN -> 0x7F, |v| clamped to 448,
+// round to nearest even on the e4m3 grid, sign kept (-0 and negative values
+// that round to zero give 0x80).
+ATTNQ_DEV uint32_t e4m3fn_encode(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fu;
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __uint_as_float(u & 0x7fffffffu);
+  a = a > 448.0f ? 448.0f : a;
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: fixed quantum 2^-9, codes 0..8
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {  // keep 3 fraction bits with round-to-nearest-even, re-bias 127 -> 7
+    uint32_t b = __float_as_uint(a);
+    b += 0x7ffffu + ((b >> 20) & 1u);
+    code = (b >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+// e4m3fn code -> fp16 bit pattern of (value * 2^-8), exact for every finite
+// code: the 7 magnitude bits land on fp16's exponent/fraction so that
+// fp16(e + 8 - 15 ... ) absorbs the bias difference as a 2^-8 factor.
+ATTNQ_DEV uint32_t e4m3_to_f16_scaled(uint32_t code) {
+  return ((code & 0x80u) << 8) | ((code & 0x7fu) << 7);
+}
+
+// Four fp8 codes packed in a dword -> two dwords of fp16 pairs (value * 2^-8).
+ATTNQ_DEV void e4m3x4_to_f16x4_scaled(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  // place byte k at the high byte of 16-bit lane k: lo = [b1 b0] -> 0xb1 00 b0 00
+  uint32_t l = __builtin_amdgcn_perm(0u, w, 0x010c000cu);  // bytes: [0]=0,[1]=b0,[2]=0,[3]=b1
+  uint32_t h = __builtin_amdgcn_perm(0u, w, 0x030c020cu);
+  lo = ((l >> 1) & 0x3f803f80u) | (l & 0x80008000u);
+  hi = ((h >> 1) & 0x3f803f80u) | (h & 0x80008000u);
+}
+
+ATTNQ_DEV int32_t int8_encode(float v) {
+  float r = __builtin_rintf(v);
+  r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+  return (int32_t)r;
+}
+
+// ---------------------------------------------------------------- reductions
+ATTNQ_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+ATTNQ_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace attnq

@@ -1,0 +1,273 @@
+// Quantizers of the path: per-head fp8 (amax -> descale -> e4m3fn codes),
+// per-128-token-block int8 (SageAttention style), and the transpose/permute
+// of V into the token order read by the prefill kernel's PV operand.
+//
+// Sources: PaddleNLP "Sage Attention Support Varlen" (varlen quant qk and
+// quant_transpose_permute v kernels); aiter "[Triton] FP8 with FA v3 API"
+// (fp8 q/k/v with per-head descales).  Arithmetic: one IEEE fp32 division
+// x / scale per element (never a reciprocal multiply), so that codes are
+// bit-identical to a plain definition of the quantizer.
+#include "kcommon.h"
+#include "launch.h"
+
+namespace attnq {
+
+// ---------------------------------------------------------------- helpers
+__global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Per-head max |x| of x [rows, heads, dim] (16-bit), accumulated as fp32 bit
+// patterns with atomicMax (valid because the values are non-negative).
+constexpr int AMAX_THREADS = 256;
+constexpr int AMAX_ROWS_PER_BLOCK = 64;
+
+__global__ __launch_bounds__(AMAX_THREADS) void k_amax_per_head(
+    const uint16_t* __restrict__ x, int rows, int heads, int dim, int is_bf16,
+    uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t s_max[1024];
+  for (int i = threadIdx.x; i < heads; i += AMAX_THREADS) s_max[i] = 0u;
+  __syncthreads();
+  const int cpr = heads * dim / 8;  // 16-byte chunks per row
+  const int row0 = blockIdx.x * AMAX_ROWS_PER_BLOCK;
+  const int nrows = min(AMAX_ROWS_PER_BLOCK, rows - row0);
+  const long n = (long)nrows * cpr;
+  const uint4* src = reinterpret_cast<const uint4*>(x) + (long)row0 * cpr;
+  float m = 0.0f;
+  int cur = -1;
+  for (long i = threadIdx.x; i < n; i += AMAX_THREADS) {
+    int h = (int)(i % cpr) * 8 / dim;
+    if (h != cur) {
+      if (cur >= 0) atomicMax(&s_max[cur], __float_as_uint(m));
+      cur = h;
+      m = 0.0f;
+    }
+    uint4 v = src[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m = fmaxf(m, fabsf(h16_to_f32(w[e] & 0xffffu, is_bf16)));
+      m = fmaxf(m, fabsf(h16_to_f32(w[e] >> 16, is_bf16)));
+    }
+  }
+  if (cur >= 0) atomicMax(&s_max[cur], __float_as_uint(m));
+  __syncthreads();
+  for (int i = threadIdx.x; i < heads; i += AMAX_THREADS)
+    if (s_max[i]) atomicMax(&amax_bits[i], s_max[i]);
+}
+
+// scale[h] = amax[h] / qmax (IEEE division), 1 where amax == 0.  `amax_in`
+// (fp32 values) overrides the in-place accumulated bits when given.
+__global__ void k_finalize_scale(const float* __restrict__ amax_in, float* scales, int heads,
+                                 float qmax) {
+  int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= heads) return;
+  float a = amax_in ? amax_in[h] : __uint_as_float(reinterpret_cast<uint32_t*>(scales)[h]);
+  scales[h] = (a == 0.0f) ? 1.0f : a / qmax;
+}
+
+// codes = e4m3fn(x / descale[head]), 8 elements per work item.
+__global__ __launch_bounds__(256) void k_quant_fp8(const uint16_t* __restrict__ x, long n_chunks,
+                                                   int heads, int dim, int is_bf16,
+                                                   const float* __restrict__ descale,
+                                                   uint8_t* __restrict__ codes) {
+  const int cpr_head = dim / 8;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks;
+       i += (long)gridDim.x * blockDim.x) {
+    int h = (int)((i / cpr_head) % heads);
+    float d = descale[h];
+    uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      uint32_t c0 = e4m3fn_encode(h16_to_f32(w[2 * p] & 0xffffu, is_bf16) / d);
+      uint32_t c1 = e4m3fn_encode(h16_to_f32(w[2 * p] >> 16, is_bf16) / d);
+      uint32_t c2 = e4m3fn_encode(h16_to_f32(w[2 * p + 1] & 0xffffu, is_bf16) / d);
+      uint32_t c3 = e4m3fn_encode(h16_to_f32(w[2 * p + 1] >> 16, is_bf16) / d);
+      out[p] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    reinterpret_cast<uint2*>(codes)[i] = make_uint2(out[0], out[1]);
+  }
+}
+
+// ---------------------------------------------------------------- int8 per block
+// One workgroup per (block j, head h, sequence b): the block's rows are
+// loaded once into registers, reduced to amax, then quantized.
+constexpr int I8_THREADS = 256;
+constexpr int I8_MAX_CHUNKS = 8;  // 128 rows * 128 dim / 8 / 256 threads
+
+__global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int dim,
+    int block_tokens, int nblk, int is_bf16, int total_tokens, int8_t* __restrict__ codes,
+    float* __restrict__ scales) {
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
+  const int r0 = s0 + j * block_tokens;
+  float* sc_out = scales + ((long)b * heads + h) * nblk + j;
+  if (r0 >= s1) {
+    if (threadIdx.x == 0) *sc_out = 0.0f;
+    return;
+  }
+  const int nrows = min(block_tokens, s1 - r0);
+  const int cpr = dim / 8;
+  const int nchunks = nrows * cpr;
+  uint4 v[I8_MAX_CHUNKS];
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < I8_MAX_CHUNKS; ++k) {
+    int c = threadIdx.x + k * I8_THREADS;
+    v[k] = make_uint4(0, 0, 0, 0);
+    if (c < nchunks) {
+      int row = c / cpr, col = (c % cpr) * 8;
+      v[k] = *reinterpret_cast<const uint4*>(x + ((long)(r0 + row) * heads + h) * dim + col);
+      uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m = fmaxf(m, fabsf(h16_to_f32(w[e] & 0xffffu, is_bf16)));
+        m = fmaxf(m, fabsf(h16_to_f32(w[e] >> 16, is_bf16)));
+      }
+    }
+  }
+  __shared__ float s_red[I8_THREADS / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float amax = s_red[0];
+#pragma unroll
+  for (int w = 1; w < I8_THREADS / 64; ++w) amax = fmaxf(amax, s_red[w]);
+  const float scale = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  if (threadIdx.x == 0) *sc_out = scale;
+#pragma unroll
+  for (int k = 0; k < I8_MAX_CHUNKS; ++k) {
+    int c = threadIdx.x + k * I8_THREADS;
+    if (c < nchunks) {
+      int row = c / cpr, col = (c % cpr) * 8;
+      uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      uint32_t out[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        uint32_t q0 = (uint32_t)int8_encode(h16_to_f32(w[2 * p] & 0xffffu, is_bf16) / scale) & 0xffu;
+        uint32_t q1 = (uint32_t)int8_encode(h16_to_f32(w[2 * p] >> 16, is_bf16) / scale) & 0xffu;
+        uint32_t q2 = (uint32_t)int8_encode(h16_to_f32(w[2 * p + 1] & 0xffffu, is_bf16) / scale) & 0xffu;
+        uint32_t q3 = (uint32_t)int8_encode(h16_to_f32(w[2 * p + 1] >> 16, is_bf16) / scale) & 0xffu;
+        out[p] = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+      }
+      *reinterpret_cast<uint2*>(codes + ((long)(r0 + row) * heads + h) * dim + col) =
+          make_uint2(out[0], out[1]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- V transpose / permute
+// V [T, H, D] -> V^T [B, H, D, S_pad].  One workgroup per (64-token tile,
+// head, sequence).  Inside each 32-token group, stored position 8g + s holds
+// token (s/4)*16 + 4g + s%4: lane group g of the PV operand then reads its 8
+// tokens as one contiguous 8-element vector.
+constexpr int VP_THREADS = 256;
+constexpr int VP_TILE = 64;
+
+__global__ __launch_bounds__(VP_THREADS) void k_v_permute(
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu, int heads, int dim,
+    int s_pad, int is_bf16, int total_tokens, int fp8, const float* __restrict__ descale,
+    void* __restrict__ out) {
+  __shared__ uint16_t s_t[128][VP_TILE + 2];  // [d][token], padded rows
+  const int t0 = blockIdx.x * VP_TILE, h = blockIdx.y, b = blockIdx.z;
+  const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
+  const int L = s1 - s0;
+  const int cpr = dim / 8;
+  for (int c = threadIdx.x; c < VP_TILE * cpr; c += VP_THREADS) {
+    int tok = c / cpr, col = (c % cpr) * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t0 + tok < L)
+      val = *reinterpret_cast<const uint4*>(v + ((long)(s0 + t0 + tok) * heads + h) * dim + col);
+    uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s_t[col + 2 * e][tok] = (uint16_t)(w[e] & 0xffffu);
+      s_t[col + 2 * e + 1][tok] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  const float ds = fp8 ? descale[h] : 1.0f;
+  const long row_base = ((long)b * heads + h) * dim;
+  for (int it = threadIdx.x; it < dim * (VP_TILE / 8); it += VP_THREADS) {
+    int d = it / (VP_TILE / 8), p0 = (it % (VP_TILE / 8)) * 8;
+    int grp = p0 / 32, g = (p0 % 32) / 8;
+    uint32_t e16[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) e16[s] = s_t[d][grp * 32 + (s / 4) * 16 + 4 * g + (s % 4)];
+    long o = (row_base + d) * s_pad + t0 + p0;
+    if (fp8) {
+      uint32_t c[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) c[s] = e4m3fn_encode(h16_to_f32(e16[s], is_bf16) / ds);
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + o) =
+          make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    } else {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) =
+          make_uint4(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
+                     e16[6] | (e16[7] << 16));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+static inline bool ok(hipError_t e) { return e == hipSuccess; }
+
+bool launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return true;
+  hipLaunchKernelGGL(k_fill_u32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return ok(hipGetLastError());
+}
+
+bool launch_amax(const void* x, int rows, int heads, int dim, bool is_bf16, uint32_t* amax_bits,
+                 hipStream_t s) {
+  if (rows <= 0) return true;
+  int grid = (rows + AMAX_ROWS_PER_BLOCK - 1) / AMAX_ROWS_PER_BLOCK;
+  hipLaunchKernelGGL(k_amax_per_head, dim3(grid), dim3(AMAX_THREADS), 0, s,
+                     static_cast<const uint16_t*>(x), rows, heads, dim, (int)is_bf16, amax_bits);
+  return ok(hipGetLastError());
+}
+
+bool launch_finalize_scale(const float* amax_in, float* scales, int heads, float qmax,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_finalize_scale, dim3((heads + 255) / 256), dim3(256), 0, s, amax_in,
+                     scales, heads, qmax);
+  return ok(hipGetLastError());
+}
+
+bool launch_quant_fp8(const void* x, long elems, int heads, int dim, bool is_bf16,
+                      const float* descale, void* codes, hipStream_t s) {
+  long n_chunks = elems / 8;
+  if (n_chunks <= 0) return true;
+  long want = (n_chunks + 255) / 256;
+  int grid = (int)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(k_quant_fp8, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                     n_chunks, heads, dim, (int)is_bf16, descale, static_cast<uint8_t*>(codes));
+  return ok(hipGetLastError());
+}
+
+bool launch_quant_int8_block(const void* x, const int32_t* cu, int batch, int heads, int dim,
+                             int block_tokens, int nblk, bool is_bf16, int total_tokens,
+                             void* codes, float* scales, hipStream_t s) {
+  if (batch <= 0 || nblk <= 0) return true;
+  hipLaunchKernelGGL(k_quant_int8_block, dim3(nblk, heads, batch), dim3(I8_THREADS), 0, s,
+                     static_cast<const uint16_t*>(x), cu, heads, dim, block_tokens, nblk,
+                     (int)is_bf16, total_tokens, static_cast<int8_t*>(codes), scales);
+  return ok(hipGetLastError());
+}
+
+bool launch_v_permute(const void* v, const int32_t* cu, int batch, int heads, int dim, int s_pad,
+                      bool is_bf16, int total_tokens, bool fp8, const float* descale, void* out,
+                      hipStream_t s) {
+  if (batch <= 0 || s_pad <= 0) return true;
+  hipLaunchKernelGGL(k_v_permute, dim3(s_pad / VP_TILE, heads, batch), dim3(VP_THREADS), 0, s,
+                     static_cast<const uint16_t*>(v), cu, heads, dim, s_pad, (int)is_bf16,
+                     total_tokens, (int)fp8, descale, out);
+  return ok(hipGetLastError());
+}
+
+}  // namespace attnq

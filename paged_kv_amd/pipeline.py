@@ -1,0 +1,192 @@
+"""Call sequences of the path over device tensors (allocation + C-ABI calls).
+
+Each function allocates its outputs with torch (device memory plumbing) and
+enqueues the library's entry points in order on the current stream; every
+step of the computation runs in libattnq's HIP kernels.  Inputs are torch
+tensors already on the GPU, with the dtypes named in include/attnq.h
+(bf16 / fp16 data, uint8 fp8 codes, int32 indices, fp32 scales).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import api as A
+
+
+def _round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return A.BF16
+    if t.dtype == torch.float16:
+        return A.FP16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Fp8Prefill:
+    """fp8 per-head quantization of Q/K/V followed by the varlen prefill
+    (the aiter fp8 flash_attn_func flow over a ragged batch)."""
+
+    def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True,
+                 out_dtype=torch.bfloat16, want_lse=False, amax=None):
+        dev = q.device
+        self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
+        self.t, self.hq, self.d = q.shape
+        self.hkv = k.shape[1]
+        self.b = cu_seqlens.numel() - 1
+        self.max_seqlen = int(max_seqlen)
+        self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        self.amax = amax  # optional (amax_q, amax_k, amax_v) from the append step
+        self.qc = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        self.kc = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+        self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_seqlen, 128)),
+                              dtype=torch.uint8, device=dev)
+        self.qs = torch.empty(self.hq, dtype=torch.float32, device=dev)
+        self.ks = torch.empty(self.hkv, dtype=torch.float32, device=dev)
+        self.vs = torch.empty(self.hkv, dtype=torch.float32, device=dev)
+        self.o = torch.empty((self.t, self.hq, self.d), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((self.hq, self.t), dtype=torch.float32, device=dev) if want_lse else None
+
+    def quantize(self):
+        dt = _dtype_code(self.q)
+        aq, ak, av = self.amax if self.amax is not None else (None, None, None)
+        A.attn_quant_qk(self.q, dt, self.cu, self.b, self.max_seqlen, self.t, self.hq, self.d,
+                        A.Q_FP8_PER_HEAD, 128, aq, self.qc, self.qs)
+        A.attn_quant_qk(self.k, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d,
+                        A.Q_FP8_PER_HEAD, 128, ak, self.kc, self.ks)
+        A.attn_quant_v_permute(self.v, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
+                               self.d, A.Q_FP8_PER_HEAD, av, self.vp, self.vs)
+
+    def attend(self):
+        A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3, A.FP8E4M3, self.qs, self.ks,
+                              self.vs, A.Q_FP8_PER_HEAD, self.cu, self.cu, self.b, self.max_seqlen,
+                              self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
+                              self.sm_scale, self.causal, self.o, _dtype_code(self.o), self.lse)
+
+    def run(self):
+        self.quantize()
+        self.attend()
+        return self.o
+
+
+class SagePrefill:
+    """SageAttention-style flow: per-128-token-block int8 Q/K, fp16 V in the
+    permuted transposed layout, int8 QK / fp16 PV prefill, fp16 output."""
+
+    def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False):
+        dev = q.device
+        self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
+        self.t, self.hq, self.d = q.shape
+        self.hkv = k.shape[1]
+        self.b = cu_seqlens.numel() - 1
+        self.max_seqlen = int(max_seqlen)
+        self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        nblk = (self.max_seqlen + 127) // 128
+        self.qc = torch.empty(q.shape, dtype=torch.int8, device=dev)
+        self.kc = torch.empty(k.shape, dtype=torch.int8, device=dev)
+        self.qs = torch.empty((self.b, self.hq, nblk), dtype=torch.float32, device=dev)
+        self.ks = torch.empty((self.b, self.hkv, nblk), dtype=torch.float32, device=dev)
+        self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_seqlen, 128)),
+                              dtype=torch.float16, device=dev)
+        self.o = torch.empty((self.t, self.hq, self.d), dtype=torch.float16, device=dev)
+        self.lse = torch.empty((self.hq, self.t), dtype=torch.float32, device=dev) if want_lse else None
+
+    def quantize(self):
+        dt = _dtype_code(self.q)
+        A.attn_quant_qk(self.q, dt, self.cu, self.b, self.max_seqlen, self.t, self.hq, self.d,
+                        A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs)
+        A.attn_quant_qk(self.k, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d,
+                        A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
+        A.attn_quant_v_permute(self.v, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
+                               self.d, A.Q_NONE, None, self.vp, None)
+
+    def attend(self):
+        A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.INT8, A.FP16, self.qs, self.ks, None,
+                              A.Q_INT8_PER_BLOCK, self.cu, self.cu, self.b, self.max_seqlen,
+                              self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
+                              self.sm_scale, self.causal, self.o, A.FP16, self.lse)
+
+    def run(self):
+        self.quantize()
+        self.attend()
+        return self.o
+
+
+class AppendRopeFp8Prefill:
+    """RoPE + paged bf16 cache write with fused per-head amax, then the fp8
+    prefill on the rotated Q/K and V (the long-context flow)."""
+
+    def __init__(self, q, k, v, cu_seqlens, kv_len_before, max_seqlen, rope_cos_sin, k_cache,
+                 v_cache, kv_indptr, kv_indices, page_size, sm_scale, causal=True, want_lse=False):
+        dev = q.device
+        self.q, self.k, self.v = q, k, v
+        self.cu, self.before = cu_seqlens, kv_len_before
+        self.cs, self.kcache, self.vcache = rope_cos_sin, k_cache, v_cache
+        self.indptr, self.indices, self.page_size = kv_indptr, kv_indices, int(page_size)
+        self.t, self.hq, self.d = q.shape
+        self.hkv = k.shape[1]
+        self.b = cu_seqlens.numel() - 1
+        self.amax = tuple(torch.empty(h, dtype=torch.float32, device=dev)
+                          for h in (self.hq, self.hkv, self.hkv))
+        self.prefill = Fp8Prefill(q, k, v, cu_seqlens, max_seqlen, sm_scale, causal,
+                                  want_lse=want_lse, amax=self.amax)
+
+    def append(self):
+        A.attn_append_kv_rope(self.q, self.k, self.v, _dtype_code(self.q), self.cu, self.before,
+                              self.b, self.t, self.hq, self.hkv, self.d, self.cs, self.cs.shape[0],
+                              self.kcache, self.vcache, self.indptr, self.indices,
+                              self.kcache.shape[0], self.page_size, *self.amax)
+
+    def run(self):
+        self.append()
+        return self.prefill.run()
+
+
+class PagedDecode:
+    """Split-KV paged fp8 decode + log-sum-exp merge."""
+
+    def __init__(self, q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices,
+                 kv_last_page_len, max_kv_len, sm_scale, want_lse=False):
+        dev = q.device
+        self.args = (q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len)
+        self.b, self.hq, self.d = q.shape
+        self.num_pages, self.page_size, self.hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+        self.max_kv_len, self.sm_scale = int(max_kv_len), float(sm_scale)
+        self.ws_bytes = A.attn_decode_paged_workspace_size(self.b, self.hq, self.d, self.max_kv_len,
+                                                           self.page_size)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((self.b, self.hq, self.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.b, self.hq), dtype=torch.float32, device=dev) if want_lse else None
+
+    def run(self):
+        A.attn_decode_paged(*self.args, self.b, self.num_pages, self.page_size, self.hq, self.hkv,
+                            self.d, self.max_kv_len, self.sm_scale, self.ws, self.ws_bytes, self.o,
+                            self.lse)
+        return self.o
+
+
+class SparseMlaDecode:
+    """MLA-absorb sparse decode over int8 cache rows with tile-128 scales."""
+
+    def __init__(self, q, kv_cache, block_table, kv_lens, sparse_indices, sm_scale=None,
+                 want_lse=False):
+        dev = q.device
+        self.q, self.cache, self.table, self.kv_lens, self.idx = q, kv_cache, block_table, kv_lens, sparse_indices
+        self.b, self.sq, self.h, dq = q.shape
+        self.topk = sparse_indices.shape[-1]
+        self.sm_scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(dq)
+        self.ws_bytes = A.attn_sparse_mla_decode_workspace_size(self.b, self.sq, self.h, self.topk)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((self.b, self.sq, self.h, 512), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.b, self.sq, self.h), dtype=torch.float32, device=dev) if want_lse else None
+
+    def run(self):
+        A.attn_sparse_mla_decode(self.q, self.cache, self.table, self.table.shape[1], self.kv_lens,
+                                 self.idx, self.topk, self.b, self.sq, self.h, self.cache.shape[0],
+                                 self.cache.shape[1], self.sm_scale, self.ws, self.ws_bytes, self.o,
+                                 self.lse)
+        return self.o

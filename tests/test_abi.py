@@ -1,0 +1,141 @@
+"""The C ABI on the CPU: the library loads, exports what include/attnq.h
+declares, and rejects bad host arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_amd as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pk.library_path()),
+                                reason="libattnq.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(\w+)\s*\(", src, flags=re.M)
+
+
+def test_header_declares_the_six_calls():
+    names = set(_declared())
+    for n in ["attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
+              "attn_decode_paged", "attn_sparse_mla_decode"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    h = ctypes.CDLL(pk.library_path())
+    for name in _declared():
+        assert hasattr(h, name), name
+    assert set(_declared()) == set(pk.api.SYMBOLS)
+
+
+def test_abi_version():
+    assert pk.abi_version() == 1
+
+
+def _err():
+    return pk.lib().attnq_last_error().decode()
+
+
+FAKE = 1 << 20          # aligned, never dereferenced: validation fails first
+
+
+def test_quant_qk_validation():
+    L = pk.lib()
+    assert L.attn_quant_qk(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 96, 0, 128, None, FAKE, FAKE, None) == -2
+    assert "head_dim" in _err()
+    assert L.attn_quant_qk(FAKE, pk.FP8E4M3, FAKE, 1, 10, 10, 2, 64, 0, 128, None, FAKE, FAKE, None) == -2
+    assert L.attn_quant_qk(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, 7, 128, None, FAKE, FAKE, None) == -1
+    assert L.attn_quant_qk(FAKE + 2, pk.BF16, FAKE, 1, 10, 10, 2, 64, 0, 128, None, FAKE, FAKE, None) == -1
+    assert "aligned" in _err()
+    assert L.attn_quant_qk(FAKE, pk.FP16, FAKE, 1, 10, 10, 2, 64, 1, 64, None, FAKE, FAKE, None) == -2
+    assert "block_tokens" in _err()
+    assert L.attn_quant_qk(FAKE, pk.FP16, None, 1, 10, 10, 2, 64, 1, 128, None, FAKE, FAKE, None) == -1
+    assert "cu_seqlens" in _err()
+
+
+def test_v_permute_validation():
+    L = pk.lib()
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_INT8_PER_BLOCK, None, FAKE, FAKE, None) == -1
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_FP8_PER_HEAD, None, FAKE, None, None) == -1
+    assert "v_scales" in _err()
+
+
+def test_append_validation():
+    L = pk.lib()
+    args = [FAKE, FAKE, FAKE, pk.BF16, FAKE, None, 1, 4, 2, 2, 64, FAKE, 8, FAKE, FAKE, FAKE, FAKE, 4, 16,
+            None, None, None, None]
+    bad = list(args)
+    bad[18] = 2048
+    assert L.attn_append_kv_rope(*bad) == -1 and "page_size" in _err()
+    bad = list(args)
+    bad[12] = 0
+    assert L.attn_append_kv_rope(*bad) == -1
+    bad = list(args)
+    bad[8], bad[9] = 1000, 1000
+    assert L.attn_append_kv_rope(*bad) == -2
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qk=pk.FP8E4M3, vd=pk.FP8E4M3, qs=FAKE, ks=FAKE, vs=FAKE,
+             mode=pk.Q_FP8_PER_HEAD, cq=FAKE, ck=FAKE, b=1, mq=8, mk=8, tq=8, tk=8, hq=4, hkv=2,
+             d=128, sc=0.1, causal=1, o=FAKE, od=pk.BF16, lse=None, st=None)
+    a.update(kw)
+    return pk.lib().attn_prefill_varlen(*a.values())
+
+
+def test_prefill_validation():
+    assert _prefill(hq=3, hkv=2) == -1 and "multiple" in _err()
+    assert _prefill(d=96) == -2
+    assert _prefill(qk=pk.INT8) == -2            # int8 codes need per-block scales
+    assert _prefill(vd=pk.BF16) == -2
+    assert _prefill(od=pk.FP8E4M3) == -2
+    assert _prefill(sc=float("inf")) == -1
+    assert _prefill(cq=None) == -1
+    assert _prefill(vs=None) == -1 and "v_scale" in _err()
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, ip=FAKE, ind=FAKE, last=FAKE, b=2, np_=10,
+             ps=16, hq=32, hkv=8, d=128, mkv=100, sc=0.1, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, st=None)
+    a.update(kw)
+    return pk.lib().attn_decode_paged(*a.values())
+
+
+def test_decode_validation():
+    assert _decode(ps=8) == -1 and "page_size" in _err()
+    assert _decode(ps=2048) == -1
+    assert _decode(d=64) == -2
+    assert _decode(hq=32, hkv=1) == -2
+    assert _decode(wsb=16) == -3 and "workspace" in _err()
+    need = pk.attn_decode_paged_workspace_size(2, 32, 128, 100, 16)
+    assert need > 0
+    assert _decode(wsb=need - 1) == -3
+    assert _decode(ws=FAKE + 8) == -1
+
+
+def _mla(**kw):
+    a = dict(q=FAKE, c=FAKE, bt=FAKE, mb=4, kl=FAKE, idx=FAKE, topk=8, b=1, sq=1, h=16, nb=8, bs=64,
+             sc=0.04, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, st=None)
+    a.update(kw)
+    return pk.lib().attn_sparse_mla_decode(*a.values())
+
+
+def test_mla_validation():
+    assert _mla(h=12) == -2 and "num_heads" in _err()
+    assert _mla(topk=0) == -1 and "topk" in _err()
+    assert _mla(bs=8) == -1 and "block_size" in _err()
+    assert _mla(bs=1040) == -1
+    assert _mla(wsb=8) == -3
+
+
+def test_python_binding_raises_with_message():
+    with pytest.raises(RuntimeError, match="head_dim"):
+        pk.attn_quant_qk(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 96, pk.Q_FP8_PER_HEAD, 128, None, FAKE,
+                         FAKE, stream=0)

@@ -1,0 +1,145 @@
+"""GPU parity of the varlen prefill through the C ABI (fp8 and SageAttention
+int8 flows): quantized inputs bit-exact, outputs within the comparison rule."""
+import math
+
+import numpy as np
+import pytest
+
+import gen
+from oracle.attention import dequant_fp8_per_head, dequant_int8_per_block, prefill_varlen
+from oracle.quant import quant_fp8_per_head, quant_int8_per_block, v_permute, as_f32
+from tests.parity import to_dev, from_dev_bits, dev_u8, decode_out, compare_outputs, compare_lse
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _fp8_flow(x, sm_scale, causal=True, lse=True):
+    from paged_kv_amd.pipeline import Fp8Prefill
+    cu = x["cu_seqlens"]
+    mx = int(np.diff(cu).max()) if len(cu) > 1 else 0
+    p = Fp8Prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(cu), mx, sm_scale,
+                   causal=causal, want_lse=lse)
+    p.run()
+    torch.cuda.synchronize()
+    return p, mx
+
+
+def _check_fp8(x, sm_scale, causal=True, label=""):
+    p, mx = _fp8_flow(x, sm_scale, causal)
+    cu = x["cu_seqlens"]
+    qc, qs = quant_fp8_per_head(x["q"], "bf16")
+    kc, ks = quant_fp8_per_head(x["k"], "bf16")
+    vc, vs = quant_fp8_per_head(x["v"], "bf16")
+    vperm, _ = v_permute(x["v"], "bf16", cu, mx, fp8=True)
+    # quantized inputs are bit-exact
+    assert np.array_equal(dev_u8(p.qc), qc) and np.array_equal(dev_u8(p.kc), kc)
+    assert np.array_equal(dev_u8(p.vp), vperm)
+    for a, b in ((p.qs, qs), (p.ks, ks), (p.vs, vs)):
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), b.view(np.uint32))
+    ref = prefill_varlen(dequant_fp8_per_head(qc, qs), dequant_fp8_per_head(kc, ks),
+                         dequant_fp8_per_head(vc, vs), cu, cu, sm_scale, causal, "bf16")
+    got = decode_out(from_dev_bits(p.o), "bf16")
+    stats = compare_outputs(got, ref["o"], ref["o_exact"], "bf16", label)
+    compare_lse(p.lse.cpu().numpy(), ref["lse"], label)
+    return stats
+
+
+def test_config1_fp8_varlen():
+    x = gen.config1()
+    st = _check_fp8(x, x["sm_scale"], True, "config1")
+    print("config1", st)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_ragged_edges(d, causal):
+    # empty, single-token, exactly one tile, one past a tile, long ragged
+    lens = [1, 0, 128, 129, 64, 65, 300]
+    x = gen.prefill_fp8_inputs(31, lens, 4, 2, d, outlier_p=0.001)
+    _check_fp8(x, 1 / math.sqrt(d), causal, f"ragged d={d} causal={causal}")
+
+
+def test_fp8_gqa_8to1():
+    x = gen.prefill_fp8_inputs(32, [513, 70], 8, 1, 128)
+    _check_fp8(x, 1 / math.sqrt(128), True, "gqa8")
+
+
+def test_fp8_deterministic():
+    x = gen.prefill_fp8_inputs(33, [200, 90], 4, 4, 128)
+    p, _ = _fp8_flow(x, 0.1)
+    a = from_dev_bits(p.o).copy()
+    p.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bits(p.o), a)
+
+
+def _sage_flow(x, sm_scale, causal=True):
+    from paged_kv_amd.pipeline import SagePrefill
+    cu = x["cu_seqlens"]
+    mx = int(np.diff(cu).max())
+    p = SagePrefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(cu), mx, sm_scale,
+                    causal=causal, want_lse=True)
+    p.run()
+    torch.cuda.synchronize()
+    return p, mx
+
+
+def _sage_ref(x, mx, sm_scale, causal, rows=None, seqs=None):
+    cu = x["cu_seqlens"]
+    qc, qs = quant_int8_per_block(x["q"], "fp16", cu, mx)
+    kc, ks = quant_int8_per_block(x["k"], "fp16", cu, mx)
+    return qc, qs, kc, ks
+
+
+@pytest.mark.parametrize("lens", [[130, 257, 1, 511], [64, 0, 700]])
+def test_sage_int8_small(lens):
+    x = gen.sage_inputs(41, lens, 8, 2, 128)
+    sm = 1 / math.sqrt(128)
+    p, mx = _sage_flow(x, sm)
+    cu = x["cu_seqlens"]
+    qc, qs, kc, ks = _sage_ref(x, mx, sm, True)
+    assert np.array_equal(p.qc.cpu().numpy(), qc) and np.array_equal(p.kc.cpu().numpy(), kc)
+    assert np.array_equal(p.qs.cpu().numpy().view(np.uint32), qs.view(np.uint32))
+    vperm, _ = v_permute(x["v"], "fp16", cu, mx, fp8=False)
+    assert np.array_equal(p.vp.cpu().numpy().view(np.uint16), vperm.view(np.uint16))
+    ref = prefill_varlen(dequant_int8_per_block(qc, qs, cu), dequant_int8_per_block(kc, ks, cu),
+                         as_f32(x["v"], "fp16").astype(np.float64), cu, cu, sm, True, "fp16")
+    got = decode_out(from_dev_bits(p.o), "fp16")
+    compare_outputs(got, ref["o"], ref["o_exact"], "fp16", f"sage {lens}")
+    compare_lse(p.lse.cpu().numpy(), ref["lse"], "sage")
+
+
+def _sampled_rows(rng, L, n=12):
+    pick = {0, L - 1, min(127, L - 1), min(128, L - 1)}
+    pick |= set(rng.integers(0, L, size=n).tolist())
+    return np.array(sorted(pick))
+
+
+def test_config2_full_size_sampled():
+    """The SageAttention workload at full size (B=8, lens U{512..4096}, 32/8
+    heads, D=128): codes and scales bit-exact everywhere, outputs on sampled
+    rows of every sequence against the oracle."""
+    x = gen.config2()
+    sm = x["sm_scale"]
+    p, mx = _sage_flow(x, sm)
+    cu = x["cu_seqlens"]
+    qc, qs, kc, ks = _sage_ref(x, mx, sm, True)
+    assert np.array_equal(p.qc.cpu().numpy(), qc) and np.array_equal(p.kc.cpu().numpy(), kc)
+    assert np.array_equal(p.qs.cpu().numpy().view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(p.ks.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    got_all = decode_out(from_dev_bits(p.o), "fp16")
+    lse_all = p.lse.cpu().numpy()
+    rng = np.random.default_rng(0)
+    v32 = as_f32(x["v"], "fp16")
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        one = np.array([0, s1 - s0], np.int32)
+        qd = dequant_int8_per_block(qc[s0:s1], qs[b:b + 1], one)
+        kd = dequant_int8_per_block(kc[s0:s1], ks[b:b + 1], one)
+        vd = v32[s0:s1].astype(np.float64)
+        rows = [(0, h, _sampled_rows(rng, s1 - s0)) for h in rng.choice(32, 3, replace=False)]
+        for (_, h, idx, o_ex, o_r, l) in prefill_varlen(qd, kd, vd, one, one, sm, True, "fp16", rows=rows):
+            compare_outputs(got_all[s0 + idx, h], o_r, o_ex, "fp16", f"c2 b={b} h={h}")
+            compare_lse(lse_all[h, s0 + idx], l, f"c2 b={b} h={h}")
