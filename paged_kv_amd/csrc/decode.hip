@@ -184,37 +184,39 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_split(const DecodeArg
   }
 }
 
-// One workgroup per sequence: O = sum_c 2^(lse_c - lse) O_c, lse = log2 sum_c 2^lse_c.
-__global__ __launch_bounds__(256) void k_decode_merge(const DecodeArgs a) {
-  const int b = blockIdx.x;
+// Merge: O = sum_c 2^(lse_c - lse) O_c, lse = log2 sum_c 2^lse_c.  One
+// 32-lane group per (sequence, q head), four d values per lane.
+constexpr int MERGE_THREADS = 128;
+
+__global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(const DecodeArgs a) {
+  const int row = blockIdx.x * (MERGE_THREADS / 32) + threadIdx.x / 32;  // b * hq + qh
+  if (row >= a.batch * a.hq) return;
+  const int b = row / a.hq;
+  const int d0 = (threadIdx.x % 32) * 4;
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
   const int npg = p1 - p0;
   const int kv_len = npg > 0 ? (npg - 1) * a.page_size + clampi(a.kv_last[b], 0, a.page_size) : 0;
   const int nc = min(a.n_chunks, (kv_len + DEC_CHUNK_TOKENS - 1) / DEC_CHUNK_TOKENS);
-  for (int it = threadIdx.x; it < a.hq * (DEC_D / 4); it += blockDim.x) {
-    const int qh = it / (DEC_D / 4), d0 = (it % (DEC_D / 4)) * 4;
-    const long row0 = ((long)b * a.hq + qh) * a.n_chunks;
-    float m = -INFINITY;
-    for (int c = 0; c < nc; ++c) m = fmaxf(m, a.ws_lse[row0 + c]);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    float tot = 0.f;
-    if (m != -INFINITY) {
-      for (int c = 0; c < nc; ++c) {
-        const float lc = a.ws_lse[row0 + c];
-        if (lc == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(lc - m);
-        tot += w;
-        const float4 o4 = *reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * DEC_D + d0);
-        acc[0] += w * o4.x; acc[1] += w * o4.y; acc[2] += w * o4.z; acc[3] += w * o4.w;
-      }
+  const long row0 = (long)row * a.n_chunks;
+  float m = -INFINITY;
+  for (int c = 0; c < nc; ++c) m = fmaxf(m, a.ws_lse[row0 + c]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != -INFINITY) {
+    for (int c = 0; c < nc; ++c) {
+      const float lc = a.ws_lse[row0 + c];
+      if (lc == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(lc - m);
+      tot += w;
+      const float4 o4 = *reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * DEC_D + d0);
+      acc[0] += w * o4.x; acc[1] += w * o4.y; acc[2] += w * o4.z; acc[3] += w * o4.w;
     }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    uint32_t w0 = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
-    uint32_t w1 = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + ((long)b * a.hq + qh) * DEC_D + d0) = make_uint2(w0, w1);
-    if (a.lse && d0 == 0)
-      a.lse[(long)b * a.hq + qh] = tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
   }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  uint32_t w0 = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
+  uint32_t w1 = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + (long)row * DEC_D + d0) = make_uint2(w0, w1);
+  if (a.lse && d0 == 0) a.lse[row] = tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
 }
 
 int decode_chunk_pages(int page_size) { return DEC_CHUNK_TOKENS / page_size; }
@@ -233,7 +235,9 @@ bool launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return true;
   hipLaunchKernelGGL(k_decode_split, dim3(a.n_chunks, a.batch), dim3(DEC_THREADS), 0, s, a);
   if (hipGetLastError() != hipSuccess) return false;
-  hipLaunchKernelGGL(k_decode_merge, dim3(a.batch), dim3(256), 0, s, a);
+  const int rows = a.batch * a.hq;
+  hipLaunchKernelGGL(k_decode_merge, dim3((rows + MERGE_THREADS / 32 - 1) / (MERGE_THREADS / 32)),
+                     dim3(MERGE_THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
 

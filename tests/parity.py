@@ -15,7 +15,12 @@ import numpy as np
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
+# lse (natural log) bound: 1e-3 absolute plus a relative term.  gfx950's fp8
+# MFMA sums its 128 products with about 2^-12.7 relative precision (measured
+# worst case 1.45e-4 of the sum of |products|), so logits -- and the lse of
+# rows dominated by large logits -- carry a relative error of that order.
 LSE_ABS = 1e-3
+LSE_REL = 4e-4
 
 
 def to_dev(x, torch_dtype=None):
@@ -79,6 +84,7 @@ def compare_lse(got: np.ndarray, want: np.ndarray, label: str = "") -> float:
     fin = np.isfinite(want)
     assert np.array_equal(fin, np.isfinite(got)), f"{label}: lse finiteness differs"
     assert np.all(got[~fin] == want[~fin]), f"{label}: -inf rows differ"
-    d = float(np.abs(got[fin] - want[fin]).max(initial=0.0))
-    assert d <= LSE_ABS, f"{label}: lse max err {d}"
-    return d
+    err = np.abs(got[fin] - want[fin])
+    tol = LSE_ABS + LSE_REL * np.abs(want[fin])
+    assert np.all(err <= tol), f"{label}: lse max err {err.max()} (worst ratio to bound {(err / tol).max():.3g})"
+    return float(err.max(initial=0.0))

@@ -143,3 +143,53 @@ def test_config2_full_size_sampled():
         for (_, h, idx, o_ex, o_r, l) in prefill_varlen(qd, kd, vd, one, one, sm, True, "fp16", rows=rows):
             compare_outputs(got_all[s0 + idx, h], o_r, o_ex, "fp16", f"c2 b={b} h={h}")
             compare_lse(lse_all[h, s0 + idx], l, f"c2 b={b} h={h}")
+
+
+def test_config5_full_size_sampled():
+    """Long fp8 prefill with RoPE + paged append at full size (S=32768, 64
+    heads, D=128, 0.1% outliers x20, page 64): for 4 sampled heads the
+    rotated Q/K, the cache rows, the fp8 codes/descales are bit-exact, and
+    sampled output rows (first, last, tile edges, random) match the oracle;
+    every output is finite."""
+    from oracle.rope import append_kv_rope
+    from paged_kv_amd.pipeline import AppendRopeFp8Prefill
+    x = gen.config5()
+    S, H, D, ps = 32768, 64, 128, x["page_size"]
+    kc = torch.zeros((x["num_pages"], ps, H, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    p = AppendRopeFp8Prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
+                             to_dev(x["kv_len_before"]), S, to_dev(x["rope_cos_sin"]), kc, vc,
+                             to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]), ps, x["sm_scale"],
+                             want_lse=True)
+    p.run()
+    torch.cuda.synchronize()
+    assert torch.isfinite(p.prefill.o.float()).all()
+    rng = np.random.default_rng(5)
+    hs = np.sort(rng.choice(H, 4, replace=False))
+    sub = lambda a: np.ascontiguousarray(a[:, hs])
+    ref = append_kv_rope(sub(x["q"]), sub(x["k"]), sub(x["v"]), "bf16", x["cu_seqlens"], x["kv_len_before"],
+                         x["rope_cos_sin"], np.zeros((x["num_pages"], ps, 4, D), np.uint16),
+                         np.zeros((x["num_pages"], ps, 4, D), np.uint16), x["kv_indptr"], x["kv_indices"], ps)
+    q_rot, k_rot = ref[0], ref[1]
+    assert np.array_equal(from_dev_bits(p.q[:, hs.tolist()]), q_rot)
+    assert np.array_equal(from_dev_bits(p.k[:, hs.tolist()]), k_rot)
+    assert np.array_equal(from_dev_bits(kc[:, :, hs.tolist()]), ref[2])
+    assert np.array_equal(from_dev_bits(vc[:, :, hs.tolist()]), ref[3])
+    qc, qs = quant_fp8_per_head(q_rot, "bf16")
+    kq, ks = quant_fp8_per_head(k_rot, "bf16")
+    vq, vs = quant_fp8_per_head(sub(x["v"]), "bf16")
+    pf = p.prefill
+    assert np.array_equal(dev_u8(pf.qc[:, hs.tolist()]), qc)
+    assert np.array_equal(dev_u8(pf.kc[:, hs.tolist()]), kq)
+    assert np.array_equal(pf.qs.cpu().numpy()[hs].view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(pf.vs.cpu().numpy()[hs].view(np.uint32), vs.view(np.uint32))
+    cu = x["cu_seqlens"]
+    qd, kd, vd = dequant_fp8_per_head(qc, qs), dequant_fp8_per_head(kq, ks), dequant_fp8_per_head(vq, vs)
+    rows = [(0, j, _sampled_rows(rng, S, 24)) for j in range(4)]
+    got_all = decode_out(from_dev_bits(pf.o[:, hs.tolist()]), "bf16")
+    lse_all = pf.lse.cpu().numpy()[hs]
+    worst = []
+    for (_, j, idx, o_ex, o_r, l) in prefill_varlen(qd, kd, vd, cu, cu, x["sm_scale"], True, "bf16", rows=rows):
+        worst.append(compare_outputs(got_all[idx, j], o_r, o_ex, "bf16", f"c5 head {hs[j]}"))
+        compare_lse(lse_all[j, idx], l, f"c5 head {hs[j]}")
+    print("config5", worst)
