@@ -3,9 +3,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define ATTNQ_DEV __device__ __forceinline__
 
 namespace attnq {
+
+// Native vector types (HIP's uint4 is a union-wrapped struct that register
+// promotion does not always see through).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- 16-bit floats
 ATTNQ_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -86,5 +93,15 @@ ATTNQ_DEV float wave_max(float v) {
 }
 
 ATTNQ_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).  Keeps
+// register-array indices constant where #pragma unroll is not honoured.
+template <int B, int E, typename F>
+ATTNQ_DEV void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 }  // namespace attnq
