@@ -6,15 +6,18 @@
 // (scale t covers nope channels [128t, 128t+128)).  K = [codes*scale | rope],
 // V = codes*scale, logit = sm_scale * q . K.
 //
-// Split phase: one workgroup (4 waves, one per SIMD) per (query row, split of
-// the index list, group of 64 heads).  Per 32-index step the workgroup gathers
-// the 32 selected rows once,
-// widens the int8 codes to fp16 (exact) into LDS twice -- token-major for the
-// QK operand and channel-major (in the PV operand's token order) for the PV
-// operand -- and each wave then serves 16 heads:
+// Split phase: one workgroup (16 waves) per (query row, 256-index split,
+// group of 64 heads).  The split's indices are resolved through block_table once,
+// into LDS.  Per 32-index step the workgroup gathers the 32 selected rows,
+// widens the int8 codes to fp16 (exact) into token-major LDS rows.  Four
+// waves serve 16 heads, split by channel tile: each owns one 128-channel tile
+// of QK and PV (the last one also the rope part) and the four exchange their
+// partial scores through LDS once per step; the PV operand (channel-major)
+// is read from the token-major rows with transposing LDS reads:
 //   S^T = K Q^T    per 128-channel tile: fp16 16x16x32 MFMA, then the tile's
 //                  scale per token in fp32; rope part: bf16 MFMA;
-//   online softmax per head (exp2, lane-local partial sums);
+//   softmax per head against a lagging reference max (exact rescale only
+//   when a step's fp16 row sum leaves range), lane-local partial sums;
 //   O^T += codes^T (P * scale_t)^T   fp16 MFMA, one P operand per tile.
 // Each split writes its normalized partial O and log2-sum-exp; the merge
 // kernel combines the splits.
@@ -30,32 +33,44 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
-constexpr int MLA_THREADS = 256;
-constexpr int MLA_HB = 1;                        // 16-head blocks per wave
-constexpr int MLA_WG_HEADS = 4 * 16 * MLA_HB;    // heads per workgroup
+constexpr int MLA_THREADS = 1024;                // 16 waves: 4 head blocks x 4 channel tiles
+constexpr int MLA_WG_HEADS = 64;                 // 4 blocks x 16 heads
 constexpr int MLA_STEP = 32;                     // indices per step
 constexpr int MLA_NOPE = 512, MLA_ROPE = 64, MLA_ROW = 656;
 constexpr int MLA_CPR = MLA_ROW / 16;            // 41 16-byte chunks per row
-constexpr int MLA_RAW = (MLA_STEP * MLA_CPR + MLA_THREADS - 1) / MLA_THREADS;  // 6
-constexpr int NAT_ROW = MLA_NOPE + 8;            // halfs per token-major row
-constexpr int T_ROW = MLA_STEP + 8;              // halfs per channel-major row
+constexpr int MLA_RAW = (MLA_STEP * MLA_CPR + MLA_THREADS - 1) / MLA_THREADS;  // 2
+constexpr int NAT_ROW = MLA_NOPE + 16;           // halfs per token row: 1056 B, 8 banks apart
 constexpr int ROPE_ROW = MLA_ROPE + 8;           // bf16 per rope row
-constexpr int MLA_MIN_TOKENS_PER_SPLIT = 256;
-constexpr int MLA_TARGET_WG = 256;
+constexpr int MLA_SPLIT_TOKENS = 512;            // indices per split (16 steps)
 constexpr float MLA_LN2 = 0.69314718055994530942f;
+// a step whose fp16 partial row sum stays at or below this keeps the
+// lagging reference max (every p <= 2^14, inside fp16)
+constexpr float MLA_TILE_SUM_MAX = 16384.0f;
 
-struct MlaLds {
+struct MlaStage {
   _Float16 nat[MLA_STEP * NAT_ROW];
-  _Float16 tr[MLA_NOPE * T_ROW];
   uint16_t rope[MLA_STEP * ROPE_ROW];
   float scale[MLA_STEP * 4];
-  int valid[MLA_STEP];
+};
+constexpr int MLA_NBUF = 2;  // staging buffers: step st computes, step st + 1 is staged
+struct MlaLds {
+  MlaStage buf[MLA_NBUF];
+  float xs[4][4][8][64];          // partial scores of the 4 channel tiles of each head block
+  int row_idx[MLA_SPLIT_TOKENS];  // cache row of each selected index, -1 if unused
 };
 
-// stored position of token r (0..31) in the PV operand order: lane group g
-// reads positions 8g..8g+7 = tokens 4g..4g+3 and 16+4g..16+4g+3
-ATTNQ_DEV int pv_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
+typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) lds_h4* lds_h4_ptr;
+
+// Transposed LDS read (ds_read_b64_tr_b16): inside each 16-lane group, lane
+// 4k + q names 4 consecutive fp16 values of row k; lane n receives value n
+// of the 4 rows (column n of the 4 x 16 block).
+ATTNQ_DEV uint2 read_tr16(const _Float16* p) {
+  const lds_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_ptr)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 // 4 int8 codes -> 4 fp16 values, exactly: 0x64XX is fp16 1024 + XX, and
 // XX = code + 128 after flipping the sign bit.
@@ -70,238 +85,235 @@ ATTNQ_DEV void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
 
 __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
   __shared__ __attribute__((aligned(16))) MlaLds L;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hb = wave & 3;  // 16-head block
+  const int t = wave >> 2;  // 128-channel tile of QK and PV (t = 3 also owns rope)
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, row = blockIdx.y;  // row = b * s_q + s
   const int b = row / a.s_q;
-  const int per = ((a.topk + a.n_split - 1) / a.n_split + MLA_STEP - 1) / MLA_STEP * MLA_STEP;
-  const int e_begin = split * per;
-  const int e_end = min(a.topk, e_begin + per);
-  const int kv_len = a.kv_lens[b];
-  const int* idx_row = a.idx + (long)row * a.topk;
-  const int head0 = blockIdx.z * MLA_WG_HEADS;     // first head of this workgroup
-  const bool wave_active = head0 + wave * 16 * MLA_HB < a.heads;
+  const int e_begin = split * MLA_SPLIT_TOKENS;
+  const int e_end = min(a.topk, e_begin + MLA_SPLIT_TOKENS);
+  const int head = blockIdx.z * MLA_WG_HEADS + hb * 16 + n;
+  const bool wave_active = blockIdx.z * MLA_WG_HEADS + hb * 16 < a.heads;
 
-  // ---- query operands: nope as fp16 (B of the fp16 MFMA), rope as bf16
-  v8h qn[MLA_HB][16];
-  v8bf qr[MLA_HB][2];
-#pragma unroll
-  for (int hb = 0; hb < MLA_HB; ++hb) {
-    const int head = head0 + (wave * MLA_HB + hb) * 16 + n;
+  // ---- resolve this split's indices to cache rows once
+  {
+    const int kv_len = a.kv_lens[b];
+    const int* idx_row = a.idx + (long)row * a.topk;
+    for (int e = threadIdx.x; e < MLA_SPLIT_TOKENS; e += MLA_THREADS) {
+      int r = -1;
+      if (e_begin + e < e_end) {
+        const int i = idx_row[e_begin + e];
+        if (i >= 0 && i < kv_len && i / a.block_size < a.max_blocks) {
+          const int blk = a.block_table[(long)b * a.max_blocks + i / a.block_size];
+          if (blk >= 0 && blk < a.num_blocks) r = blk * a.block_size + i % a.block_size;
+        }
+      }
+      L.row_idx[e] = r;
+    }
+  }
+
+  // ---- query operands of this wave's nope tile (fp16) and, for t = 3, rope (bf16)
+  v8h qn[4];
+  v8bf qr[2];
+  {
     const bool have = head < a.heads;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)row * a.heads + head) * (MLA_NOPE + MLA_ROPE);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int m = 0; m < 4; ++m) {
+      const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 128 * t + 32 * g + 8 * m) : u32x4{0u, 0u, 0u, 0u};
+      v8h h;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint4 w = have ? *reinterpret_cast<const uint4*>(qp + 128 * t + 32 * g + 8 * m) : make_uint4(0, 0, 0, 0);
-        uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        v8h h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          h[2 * e] = (_Float16)bf16_to_f32(ww[e] & 0xffffu);
-          h[2 * e + 1] = (_Float16)bf16_to_f32(ww[e] >> 16);
-        }
-        qn[hb][4 * t + m] = h;
+      for (int e = 0; e < 4; ++e) {
+        h[2 * e] = (_Float16)bf16_to_f32(w[e] & 0xffffu);
+        h[2 * e + 1] = (_Float16)bf16_to_f32(w[e] >> 16);
       }
+      qn[m] = h;
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      uint4 w = have ? *reinterpret_cast<const uint4*>(qp + MLA_NOPE + 16 * g + 8 * m) : make_uint4(0, 0, 0, 0);
-      qr[hb][m] = __builtin_bit_cast(v8bf, w);
+      const u32x4 w = (have && t == 3) ? *reinterpret_cast<const u32x4*>(qp + MLA_NOPE + 16 * g + 8 * m)
+                                       : u32x4{0u, 0u, 0u, 0u};
+      qr[m] = __builtin_bit_cast(v8bf, w);
     }
   }
+  __syncthreads();  // row_idx visible
 
-  v4f oacc[MLA_HB][MLA_NOPE / 16];
+  v4f oacc[8];  // O^T for channels [128 t, 128 t + 128)
 #pragma unroll
-  for (int hb = 0; hb < MLA_HB; ++hb)
-#pragma unroll
-    for (int db = 0; db < MLA_NOPE / 16; ++db) oacc[hb][db] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run[MLA_HB], l_run[MLA_HB];
-#pragma unroll
-  for (int hb = 0; hb < MLA_HB; ++hb) {
-    m_run[hb] = -INFINITY;
-    l_run[hb] = 0.f;
-  }
+  for (int db = 0; db < 8; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  // reference max (log2 units); -inf until set so the first step's p are
+  // inf/NaN and force the exact path
+  float m_ref = -INFINITY, l_run = 0.f;
+  const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
 
-  // ---- gather of one step's rows into registers
-  uint4 raw[MLA_RAW];
-  auto row_ptr = [&](int e, bool& valid) -> const uint8_t* {
-    valid = false;
-    if (e >= e_end) return nullptr;
-    const int i = idx_row[e];
-    if (i < 0 || i >= kv_len) return nullptr;
-    const int bi = i / a.block_size;
-    if (bi >= a.max_blocks) return nullptr;
-    const int blk = a.block_table[(long)b * a.max_blocks + bi];
-    if (blk < 0 || blk >= a.num_blocks) return nullptr;
-    valid = true;
-    return a.cache + ((long)blk * a.block_size + i % a.block_size) * MLA_ROW;
-  };
-  auto load_step = [&](int e0) {
-#pragma unroll
-    for (int k = 0; k < MLA_RAW; ++k) {
+  // ---- staging: chunk c of a step = (row c % 32, 16-byte column c / 32).
+  // The rows of step st + 1 are gathered into registers while step st computes.
+  u32x4 raw[MLA_RAW];
+  auto gather = [&](int st) {
+    static_for<0, MLA_RAW>([&](auto ki) {
+      constexpr int k = decltype(ki)::value;
       const int c = threadIdx.x + k * MLA_THREADS;
-      raw[k] = make_uint4(0, 0, 0, 0);
+      raw[k] = u32x4{0u, 0u, 0u, 0u};
       if (c < MLA_STEP * MLA_CPR) {
-        bool v;
-        const uint8_t* p = row_ptr(e0 + c / MLA_CPR, v);
-        if (v) raw[k] = *reinterpret_cast<const uint4*>(p + (c % MLA_CPR) * 16);
+        const int r = L.row_idx[st * MLA_STEP + (c % MLA_STEP)];
+        if (r >= 0) raw[k] = *reinterpret_cast<const u32x4*>(a.cache + (long)r * MLA_ROW + (c / MLA_STEP) * 16);
       }
-    }
+    });
   };
-  auto store_step = [&](int e0) {
-#pragma unroll
-    for (int k = 0; k < MLA_RAW; ++k) {
+  auto stage = [&](MlaStage& B) {
+    static_for<0, MLA_RAW>([&](auto ki) {
+      constexpr int k = decltype(ki)::value;
       const int c = threadIdx.x + k * MLA_THREADS;
-      if (c >= MLA_STEP * MLA_CPR) continue;
-      const int r = c / MLA_CPR, col = (c % MLA_CPR) * 16;
-      const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
-      if (col < MLA_NOPE) {
-        uint32_t h[8];
+      if (c < MLA_STEP * MLA_CPR) {
+        const int r = c % MLA_STEP, col = (c / MLA_STEP) * 16;
+        if (col < MLA_NOPE) {
+          uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) i8x4_to_f16x4(w[e], h[2 * e], h[2 * e + 1]);
-        uint4* dn = reinterpret_cast<uint4*>(&L.nat[r * NAT_ROW + col]);
-        dn[0] = make_uint4(h[0], h[1], h[2], h[3]);
-        dn[1] = make_uint4(h[4], h[5], h[6], h[7]);
-        const int pos = pv_pos(r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          L.tr[(col + 2 * e) * T_ROW + pos] = __builtin_bit_cast(_Float16, (uint16_t)(h[e] & 0xffffu));
-          L.tr[(col + 2 * e + 1) * T_ROW + pos] = __builtin_bit_cast(_Float16, (uint16_t)(h[e] >> 16));
+          for (int e = 0; e < 4; ++e) i8x4_to_f16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
+          u32x4* dn = reinterpret_cast<u32x4*>(&B.nat[r * NAT_ROW + col]);
+          dn[0] = u32x4{h[0], h[1], h[2], h[3]};
+          dn[1] = u32x4{h[4], h[5], h[6], h[7]};
+        } else if (col < MLA_NOPE + 2 * MLA_ROPE) {
+          *reinterpret_cast<u32x4*>(&B.rope[r * ROPE_ROW + (col - MLA_NOPE) / 2]) = raw[k];
+        } else {
+          *reinterpret_cast<u32x4*>(&B.scale[r * 4]) = raw[k];  // zero for unused rows
         }
-      } else if (col < MLA_NOPE + 2 * MLA_ROPE) {
-        *reinterpret_cast<uint4*>(&L.rope[r * ROPE_ROW + (col - MLA_NOPE) / 2]) = raw[k];
-      } else {
-        *reinterpret_cast<uint4*>(&L.scale[r * 4]) = raw[k];
-        bool v;
-        row_ptr(e0 + r, v);
-        L.valid[r] = v ? 1 : 0;
       }
-    }
+    });
   };
 
+  // Pipeline: step st computes on buffer st % 2.  Between the two barriers of
+  // step st the workgroup stages step st + 1 (gathered into registers during
+  // step st - 1) into the other buffer -- free because every wave finished
+  // the PV of step st - 1 before the first barrier -- and gathers step st + 2.
   const int nsteps = e_end > e_begin ? (e_end - e_begin + MLA_STEP - 1) / MLA_STEP : 0;
-  if (nsteps > 0) load_step(e_begin);
-  for (int st = 0; st < nsteps; ++st) {
-    const int e0 = e_begin + st * MLA_STEP;
-    if (st > 0) __syncthreads();  // previous step's LDS reads are done
-    store_step(e0);
+  if (nsteps > 0) {
+    gather(0);
+    stage(L.buf[0]);
+    if (nsteps > 1) gather(1);
     __syncthreads();
-    if (st + 1 < nsteps) load_step(e0 + MLA_STEP);
-    if (!wave_active) continue;
-
-    // ---- S^T for the two 16-token blocks, lane (n, g): tokens 16j + 4g + r, head n
-    float sv[MLA_HB][2][4];
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    MlaStage& B = L.buf[st % MLA_NBUF];
+    float (*xs)[4][8][64] = L.xs;
+    // ---- partial S^T of this wave's tile, lane (n, g): tokens 16j + 4g + r, head n
+    float sp[2][4];
+    if (wave_active) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float sacc[MLA_HB][4];
-      v4f racc[MLA_HB];
-#pragma unroll
-      for (int hb = 0; hb < MLA_HB; ++hb) {
-        racc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[hb][r] = 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v4f acc[MLA_HB];
-#pragma unroll
-        for (int hb = 0; hb < MLA_HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) {
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const v8h kop = *reinterpret_cast<const v8h*>(&L.nat[(16 * j + n) * NAT_ROW + 128 * t + 32 * g + 8 * m]);
-#pragma unroll
-          for (int hb = 0; hb < MLA_HB; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qn[hb][4 * t + m], acc[hb], 0, 0, 0);
+          const v8h kop = *reinterpret_cast<const v8h*>(&B.nat[(16 * j + n) * NAT_ROW + 128 * t + 32 * g + 8 * m]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qn[m], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float sc = L.scale[(16 * j + 4 * g + r) * 4 + t];
+        for (int r = 0; r < 4; ++r) sp[j][r] = B.scale[(16 * j + 4 * g + r) * 4 + t] * acc[r];
+        if (t == 3) {
+          v4f racc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int hb = 0; hb < MLA_HB; ++hb) sacc[hb][r] += sc * acc[hb][r];
+          for (int m = 0; m < 2; ++m) {
+            const v8bf kop = *reinterpret_cast<const v8bf*>(&B.rope[(16 * j + n) * ROPE_ROW + 16 * g + 8 * m]);
+            racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[m], racc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sp[j][r] += racc[r];
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const v8bf kop = *reinterpret_cast<const v8bf*>(&L.rope[(16 * j + n) * ROPE_ROW + 16 * g + 8 * m]);
-#pragma unroll
-        for (int hb = 0; hb < MLA_HB; ++hb)
-          racc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[hb][m], racc[hb], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) xs[hb][t][4 * j + r][lane] = sp[j][r];
       }
+    }
+    __syncthreads();  // scores exchanged; the PV of step st - 1 is done everywhere
+    // stage step st + 1 (gathered during step st - 1), gather step st + 2
+    if (st + 1 < nsteps) stage(L.buf[(st + 1) % MLA_NBUF]);
+    if (st + 2 < nsteps) gather(st + 2);
+    if (!wave_active) {
+      __syncthreads();
+      continue;
+    }
+    float s[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = L.valid[16 * j + 4 * g + r] != 0;
-#pragma unroll
-        for (int hb = 0; hb < MLA_HB; ++hb)
-          sv[hb][j][r] = valid ? (sacc[hb][r] + racc[hb][r]) * a.sm_scale_log2 : -INFINITY;
+        const float tot = (xs[hb][0][4 * j + r][lane] + xs[hb][1][4 * j + r][lane]) +
+                          (xs[hb][2][4 * j + r][lane] + xs[hb][3][4 * j + r][lane]);
+        s[j][r] = L.row_idx[st * MLA_STEP + 16 * j + 4 * g + r] >= 0 ? tot * a.sm_scale_log2 : -INFINITY;
       }
-    }
-    // ---- online softmax per head
-    float p[MLA_HB][8];
-    float alpha[MLA_HB];
+
+    // ---- softmax against a lagging reference max (the four waves of a
+    // head block compute identical values); exact path when a step would
+    // leave fp16 range or no reference exists yet
+    float p[8];
+    float lt = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < MLA_HB; ++hb) {
+    for (int sl = 0; sl < 8; sl += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4] - m_ref);
+      const float p1 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4 + 1] - m_ref);
+      p[sl] = p0;
+      p[sl + 1] = p1;
+      lt = __builtin_amdgcn_fdot2(__builtin_convertvector(v2f{p0, p1}, v2h), ones, lt, false);
+    }
+    if (__ballot(!(lt <= MLA_TILE_SUM_MAX))) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) mx = fmaxf(mx, sv[hb][sl / 4][sl % 4]);
+      for (int sl = 0; sl < 8; ++sl) mx = fmaxf(mx, s[sl / 4][sl % 4]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[hb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[hb] = __builtin_amdgcn_exp2f(m_run[hb] - m_use);
-      m_run[hb] = m_new;
-      float rs = 0.f;
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        p[hb][sl] = __builtin_amdgcn_exp2f(sv[hb][sl / 4][sl % 4] - m_use);
-        rs += p[hb][sl];
-      }
-      l_run[hb] = l_run[hb] * alpha[hb] + rs;
-    }
-    // ---- O^T += codes^T (P * scale_t)^T, one P operand per 128-channel tile
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      const float mu = m_new == -INFINITY ? 0.0f : m_new;
+      lt = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      v8h pk[MLA_HB];
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const float sc = L.scale[((sl / 4) * 16 + 4 * g + (sl % 4)) * 4 + t];
-#pragma unroll
-        for (int hb = 0; hb < MLA_HB; ++hb) pk[hb][sl] = (_Float16)(p[hb][sl] * sc);
-      }
-#pragma unroll
-      for (int dbt = 0; dbt < 8; ++dbt) {
-        const int db = 8 * t + dbt;
-        const v8h vop = *reinterpret_cast<const v8h*>(&L.tr[(16 * db + n) * T_ROW + 8 * g]);
-#pragma unroll
-        for (int hb = 0; hb < MLA_HB; ++hb) {
-          oacc[hb][db] *= alpha[hb];
-          oacc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk[hb], oacc[hb][db], 0, 0, 0);
-        }
-        // keep operand loads next to their MFMAs (bounded live ranges)
-        if (dbt & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int sl = 0; sl < 8; sl += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4] - mu);
+        const float p1 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4 + 1] - mu);
+        p[sl] = p0;
+        p[sl + 1] = p1;
+        lt = __builtin_amdgcn_fdot2(__builtin_convertvector(v2f{p0, p1}, v2h), ones, lt, false);
       }
     }
+    l_run += lt;
+
+    // ---- O^T += codes^T (P * scale_t)^T for this wave's tile.  Slot sl of
+    // lane group g is token (sl / 4) * 16 + 4g + sl % 4; the codes^T operand
+    // comes from the token-major rows through two transposed reads.
+    v8h pk;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      pk[sl] = (_Float16)(p[sl] * B.scale[((sl / 4) * 16 + 4 * g + (sl % 4)) * 4 + t]);
+    // address lane (g, 4k + q) names token (4g + k) (+16), channels 4q..4q+3 of the d-block
+    const int tr_row = 4 * g + (n >> 2), tr_col = 4 * (n & 3);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int c0 = 128 * t + 16 * db + tr_col;
+      const uint2 lo = read_tr16(&B.nat[tr_row * NAT_ROW + c0]);
+      const uint2 hi = read_tr16(&B.nat[(16 + tr_row) * NAT_ROW + c0]);
+      const v8h vop = __builtin_bit_cast(v8h, u32x4{lo.x, lo.y, hi.x, hi.y});
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[db], 0, 0, 0);
+    }
+    __syncthreads();  // step st + 1 staged; exchange buffer free again
   }
   if (!wave_active) return;
-  // ---- partial result of this split
+  // ---- partial result of this split: normalized O and log2-sum-exp
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (head < a.heads) {
+    const long prow = ((long)row * a.n_split + split) * a.heads + head;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int hb = 0; hb < MLA_HB; ++hb) {
-    const int head = head0 + (wave * MLA_HB + hb) * 16 + n;
-    float l = l_run[hb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (head < a.heads) {
-      const long prow = ((long)row * a.n_split + split) * a.heads + head;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-      for (int db = 0; db < MLA_NOPE / 16; ++db) {
-        float4 o4 = make_float4(oacc[hb][db][0] * inv, oacc[hb][db][1] * inv, oacc[hb][db][2] * inv,
-                                oacc[hb][db][3] * inv);
-        *reinterpret_cast<float4*>(a.ws_o + prow * MLA_NOPE + db * 16 + 4 * g) = o4;
-      }
-      if (g == 0) a.ws_lse[prow] = l > 0.f ? m_run[hb] + __log2f(l) : -INFINITY;
+    for (int db = 0; db < 8; ++db) {
+      const v4f o4 = oacc[db] * inv;
+      *reinterpret_cast<v4f*>(a.ws_o + prow * MLA_NOPE + 128 * t + db * 16 + 4 * g) = o4;
     }
+    if (g == 0 && t == 0) a.ws_lse[prow] = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
   }
 }
 
@@ -332,12 +344,7 @@ __global__ __launch_bounds__(128) void k_mla_merge(const MlaArgs a) {
   if (a.lse && threadIdx.x == 0) a.lse[rh] = tot > 0.f ? (m + __log2f(tot)) * MLA_LN2 : -INFINITY;
 }
 
-int mla_n_split(int topk) {
-  // enough splits to fill the chip for small batches, never fewer than
-  // MLA_MIN_TOKENS_PER_SPLIT indices per split
-  int s = (topk + MLA_MIN_TOKENS_PER_SPLIT - 1) / MLA_MIN_TOKENS_PER_SPLIT;
-  return s < 1 ? 1 : s;
-}
+int mla_n_split(int topk) { return (topk + MLA_SPLIT_TOKENS - 1) / MLA_SPLIT_TOKENS; }
 
 size_t mla_workspace_bytes(int batch, int s_q, int heads, int topk) {
   const size_t rows = (size_t)batch * s_q * mla_n_split(topk) * heads;
