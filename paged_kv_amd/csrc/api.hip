@@ -196,6 +196,11 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   REQUIRE(batch >= 0 && max_seqlen_q >= 0 && max_seqlen_k >= 0 && total_q >= 0 && total_k >= 0,
           ATTNQ_EINVAL, "sizes must be >= 0");
   REQUIRE(max_seqlen_q <= 65535 * 128, ATTNQ_EINVAL, "max_seqlen_q too large");
+  // K and V^T tiles are addressed with 32-bit byte offsets from the start of
+  // one (sequence, kv head)
+  REQUIRE((long)max_seqlen_k * num_kv_heads * head_dim < (1L << 31) &&
+              (long)round_up(max_seqlen_k, 128) * head_dim * 2 < (1L << 31),
+          ATTNQ_EUNSUPPORTED, "one sequence's K (max_seqlen_k * num_kv_heads * head_dim bytes) must stay below 2 GiB");
   REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
   REQUIRE_PTR(cu_seqlens_q, 4);
   REQUIRE_PTR(cu_seqlens_k, 4);

@@ -35,90 +35,75 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_BM = 128;  // queries per workgroup (4 waves x 32)
 constexpr int PF_BN = 64;   // keys per tile
+constexpr int PF_NST = 3;   // LDS stages of the DMA ring (two tiles in flight)
 constexpr float PF_LN2 = 0.69314718055994530942f;
+// buffer descriptor word 3 for untyped 32-bit accesses
+constexpr int PF_RSRC_W3 = 0x00020000;
 
-template <int D>
-struct PfLds {
-  static constexpr int KROW = D + 16;            // bytes per staged K row
-  static constexpr int VROW = PF_BN * 2 + 16;    // bytes per staged V^T row (fp16)
-  static constexpr int KBYTES = PF_BN * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS tile geometry.  Rows are unpadded; the 16-byte chunk c of row r sits at
+// chunk position c ^ swizzle(r), so that the 8 lanes an LDS b128 pass serves
+// (rows n..n+7 of one chunk column) hit 8 distinct bank groups, and the
+// direct loads (64 lanes x 16 contiguous bytes) write linearly.
+template <int D, bool V_F8>
+struct PfGeo {
+  static constexpr int K_CH = D / 16;                  // chunks per K row (codes)
+  static constexpr int KBYTES = PF_BN * D;             // one K tile
+  static constexpr int VBYTES = D * PF_BN * 2;         // one V^T tile (fp16, 128-byte rows)
+  static constexpr int NKD = KBYTES / 1024 / 4;        // K direct loads per wave per tile
+  static constexpr int NVD = V_F8 ? 0 : VBYTES / 1024 / 4;  // V^T direct loads per wave per tile
+  static constexpr int NV_ST = V_F8 ? 2 : PF_NST;      // V^T stages (fp8 V is widened through registers)
+  static constexpr int VC = V_F8 ? D * PF_BN / 16 / PF_THREADS : 0;  // fp8 V^T u32x4 per thread
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = PF_NST * KBYTES;
+  static constexpr int LDS = V_OFF + NV_ST * VBYTES;
+  static ATTNQ_DEV int ksw(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  static ATTNQ_DEV int vsw(int r) { return (r >> 1) & 7; }
 };
 
-// Staging registers for one 64-key tile (K rows and V^T rows).
-template <int D, bool V_F8>
-struct PfStage {
-  static constexpr int V_ELEM = V_F8 ? 1 : 2;
-  static constexpr int KC = PF_BN * D / 16 / PF_THREADS;           // u32x4 per thread (K)
-  static constexpr int VC = D * PF_BN * V_ELEM / 16 / PF_THREADS;  // u32x4 per thread (V^T)
-  u32x4 k[KC];
-  u32x4 v[VC];
-};
-
-template <int D, bool V_F8>
-ATTNQ_DEV PfStage<D, V_F8> pf_load(const uint8_t* kbase, long kstride, const uint8_t* vbase,
-                                   long vrow_stride, int kt, int Lk) {
-  using S = PfStage<D, V_F8>;
-  S r;
-  static_for<0, S::KC>([&](auto ci) {
-    constexpr int c = decltype(ci)::value;
-    const int idx = threadIdx.x + c * PF_THREADS;
-    const int row = idx / (D / 16), col = (idx % (D / 16)) * 16;
-    // rows past the sequence end re-read the last row (never out of bounds);
-    // their scores are masked before the softmax
-    const int key = min(kt * PF_BN + row, Lk - 1);
-    r.k[c] = *reinterpret_cast<const u32x4*>(kbase + key * kstride + col);
-  });
-  static_for<0, S::VC>([&](auto ci) {
-    constexpr int c = decltype(ci)::value;
-    const int idx = threadIdx.x + c * PF_THREADS;
-    constexpr int CPR = PF_BN * S::V_ELEM / 16;
-    const int row = idx / CPR, col = (idx % CPR) * 16;
-    r.v[c] = *reinterpret_cast<const u32x4*>(vbase + row * vrow_stride + (long)kt * PF_BN * S::V_ELEM + col);
-  });
-  return r;
+ATTNQ_DEV __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, PF_RSRC_W3);
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order), N a compile-time constant.
+template <int N>
+ATTNQ_DEV void pf_wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4]=7, lgkmcnt[11:8]=15
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// 16 fp8 codes (one u32x4) -> 16 fp16 values (exact), two u32x4.
+ATTNQ_DEV void pf_widen_fp8(const u32x4 w, u32x4& lo, u32x4& hi) {
+  lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false));
+  lo[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true));
+  lo[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false));
+  lo[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true));
+  hi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2], 1.0f, false));
+  hi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2], 1.0f, true));
+  hi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[3], 1.0f, false));
+  hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[3], 1.0f, true));
+}
+
+// Direct loads of one tile: K rows into the K stage and (fp16 V) V^T rows into
+// the V stage; this wave's share is blocks [wave*N, wave*N + N) of 1 KB.
 template <int D, bool V_F8>
-ATTNQ_DEV void pf_store(const PfStage<D, V_F8> r, uint8_t* st) {
-  using S = PfStage<D, V_F8>;
-  using L = PfLds<D>;
-  uint8_t* sk = st;
-  uint8_t* sv = st + L::KBYTES;
-  static_for<0, S::KC>([&](auto ci) {
-    constexpr int c = decltype(ci)::value;
-    const int idx = threadIdx.x + c * PF_THREADS;
-    const int row = idx / (D / 16), col = (idx % (D / 16)) * 16;
-    *reinterpret_cast<u32x4*>(sk + row * L::KROW + col) = r.k[c];
-  });
-  static_for<0, S::VC>([&](auto ci) {
-    constexpr int c = decltype(ci)::value;
-    const int idx = threadIdx.x + c * PF_THREADS;
-    constexpr int CPR = PF_BN * S::V_ELEM / 16;
-    const int row = idx / CPR, colb = (idx % CPR) * 16;
-    if constexpr (V_F8) {
-      // 16 fp8 codes -> 16 fp16 (exact) -> 32 bytes
-      u32x4 lo, hi;
-      lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][0], 1.0f, false));
-      lo[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][0], 1.0f, true));
-      lo[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][1], 1.0f, false));
-      lo[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][1], 1.0f, true));
-      hi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][2], 1.0f, false));
-      hi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][2], 1.0f, true));
-      hi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][3], 1.0f, false));
-      hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[c][3], 1.0f, true));
-      uint8_t* dst = sv + row * L::VROW + colb * 2;
-      *reinterpret_cast<u32x4*>(dst) = lo;
-      *reinterpret_cast<u32x4*>(dst + 16) = hi;
-    } else {
-      *reinterpret_cast<u32x4*>(sv + row * L::VROW + colb) = r.v[c];
-    }
-  });
+ATTNQ_DEV void pf_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const uint32_t* kvo,
+                      const uint32_t* vvo, uint32_t k_soff, uint32_t v_soff, uint8_t* kdst, uint8_t* vdst) {
+  using G = PfGeo<D, V_F8>;
+#pragma unroll
+  for (int j = 0; j < G::NKD; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kdst + j * 1024), 16, kvo[j], k_soff, 0, 0);
+#pragma unroll
+  for (int j = 0; j < G::NVD; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vdst + j * 1024), 16, vvo[j], v_soff, 0, 0);
 }
 
 // A tile whose fp16 partial row sum (16 scores per lane) stays at or below
@@ -128,13 +113,13 @@ constexpr float PF_TILE_SUM_MAX = 16384.0f;
 
 template <int D, bool QK_I8, bool V_F8, bool O_BF16>
 __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) {
-  using L = PfLds<D>;
-  using Stage = PfStage<D, V_F8>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using G = PfGeo<D, V_F8>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int h = blockIdx.x % a.hq, b = blockIdx.x / a.hq;
+  const int h = __builtin_amdgcn_readfirstlane(blockIdx.x % a.hq);
+  const int b = __builtin_amdgcn_readfirstlane(blockIdx.x / a.hq);
   const int tile = gridDim.y - 1 - blockIdx.y;
   const int q0 = clampi(a.cu_q[b], 0, a.total_q), q1 = clampi(a.cu_q[b + 1], q0, a.total_q);
   const int k0 = clampi(a.cu_k[b], 0, a.total_k), k1 = clampi(a.cu_k[b + 1], k0, a.total_k);
@@ -143,7 +128,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   const int Lq = min(q1 - q0, a.max_q), Lk = min(k1 - k0, a.max_k);
   const int qs = tile * PF_BM;
   if (qs >= Lq) return;
-  const int hk = h / (a.hq / a.hkv);
+  const int hk = __builtin_amdgcn_readfirstlane(h / (a.hq / a.hkv));
   const int off = Lk - Lq;  // bottom-right causal alignment
   int kend = Lk;
   if (a.causal) kend = min(Lk, qs + PF_BM + off);
@@ -172,12 +157,72 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   if constexpr (QK_I8) q_sc = a.q_scale[((long)b * a.hq + h) * a.nblk_q + tile];
   else q_sc = a.q_scale[h];
   const float k_sc_head = QK_I8 ? 0.0f : a.k_scale[hk];
+  // int8: one scale per 128-key block, read through the scalar cache (the
+  // constant address space) so no vector-memory wait joins the tile loads
+  const __attribute__((address_space(4))) float* k_sc_blk =
+      (const __attribute__((address_space(4))) float*)(uintptr_t)(a.k_scale + ((long)b * a.hkv + hk) * a.nblk_k);
   const float base_fold = a.sm_scale_log2 * q_sc;
 
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)k0 * a.hkv + hk) * D;
+  // ---- tile sources as buffer descriptors: K rows of this (sequence, kv head)
+  // with the range ending at the last key (rows past it arrive as zeros), and
+  // the padded V^T block of this (sequence, kv head).
   const long kstride = (long)a.hkv * D;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)b * a.hkv + hk) * D * (long)a.s_pad * Stage::V_ELEM;
-  const long vrow_stride = (long)a.s_pad * Stage::V_ELEM;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)k0 * a.hkv + hk) * D;
+  const __amdgpu_buffer_rsrc_t krs = pf_rsrc(kbase, Lk > 0 ? (uint32_t)((Lk - 1) * kstride + D) : 0u);
+  const long vrow = (long)a.s_pad * (V_F8 ? 1 : 2);  // bytes per V^T row
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)b * a.hkv + hk) * D * vrow;
+  const __amdgpu_buffer_rsrc_t vrs = pf_rsrc(vbase, (uint32_t)(D * vrow));
+
+  // per-lane byte offsets of the direct loads: wave w fills 1 KB blocks
+  // w*N + j of the K (and V^T) stage; lane i of a block writes its chunk i
+  uint32_t kvo[G::NKD];
+#pragma unroll
+  for (int j = 0; j < G::NKD; ++j) {
+    const int blk = wave * G::NKD + j;
+    const int r = blk * (1024 / D) + lane / G::K_CH;
+    const int c = (lane % G::K_CH) ^ G::ksw(r);
+    kvo[j] = (uint32_t)(r * kstride + c * 16);
+  }
+  uint32_t vvo[G::NVD > 0 ? G::NVD : 1];
+#pragma unroll
+  for (int j = 0; j < G::NVD; ++j) {
+    const int blk = wave * G::NVD + j;
+    const int r = blk * 8 + lane / 8;
+    const int c = (lane % 8) ^ G::vsw(r);
+    vvo[j] = (uint32_t)(r * vrow + c * 16);
+  }
+  // fp8 V^T: 16 codes per load, widened to fp16 on the way into LDS
+  u32x4 vreg[G::VC > 0 ? G::VC : 1];
+  auto vload = [&](int t) {
+    static_for<0, G::VC>([&](auto ci) {
+      constexpr int c = decltype(ci)::value;
+      const int idx = threadIdx.x + c * PF_THREADS;
+      vreg[c] = *reinterpret_cast<const u32x4*>(vbase + (long)t * PF_BN + (idx >> 2) * vrow + (idx & 3) * 16);
+    });
+  };
+  auto vstore = [&](int stage) {
+    static_for<0, G::VC>([&](auto ci) {
+      constexpr int c = decltype(ci)::value;
+      const int idx = threadIdx.x + c * PF_THREADS;
+      const int r = idx >> 2, j = idx & 3;
+      u32x4 lo, hi;
+      pf_widen_fp8(vreg[c], lo, hi);
+      uint8_t* row = smem + G::V_OFF + stage * G::VBYTES + r * 128;
+      *reinterpret_cast<u32x4*>(row + ((2 * j) ^ G::vsw(r)) * 16) = lo;
+      *reinterpret_cast<u32x4*>(row + ((2 * j + 1) ^ G::vsw(r)) * 16) = hi;
+    });
+  };
+
+  const uint32_t ktile_bytes = (uint32_t)(PF_BN * kstride);
+  // this wave's 1 KB blocks of stage st
+  auto kdst = [&](int st) { return smem + G::K_OFF + st * G::KBYTES + wave * G::NKD * 1024; };
+  auto vdst = [&](int st) { return smem + G::V_OFF + st * G::VBYTES + wave * G::NVD * 1024; };
+
+  // per-lane LDS read offsets (swizzled); kb / db add whole 16-row blocks
+  const int kr0 = (D == 128 ? n * 128 + (((2 * g) ^ G::ksw(n)) * 16) : n * 64 + ((g ^ G::ksw(n)) * 16));
+  const int kr1 = n * 128 + (((2 * g + 1) ^ G::ksw(n)) * 16);  // D == 128 only
+  const int vr0 = n * 128 + ((g ^ G::vsw(n)) * 16);
+  const int vr1 = n * 128 + (((4 + g) ^ G::vsw(n)) * 16);
 
   // ---- accumulators
   v4f oacc[D / 16][2];
@@ -191,26 +236,42 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   float l_run[2] = {0.f, 0.f};              // lane-local partial row sums
   const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
 
-  Stage cur;
-  if (n_kt > 0) cur = pf_load<D, V_F8>(kbase, kstride, vbase, vrow_stride, 0, Lk);
+  // ---- prologue: tiles 0 and 1 in flight
+  constexpr int NPEND = G::NKD + G::NVD;  // direct loads per wave per tile
+  if (n_kt > 0) {
+    pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
+    if constexpr (V_F8) vload(0);
+    if (n_kt > 1) pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
+  }
+  int kst = 0;  // K (and DMA'd V^T) stage of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
-    uint8_t* st = smem + (kt & 1) * L::STAGE;
-    pf_store<D, V_F8>(cur, st);
+    if constexpr (V_F8) vstore(kt & 1);
+    // tile kt landed (only tile kt+1's direct loads may still be in flight)
+    if (kt + 1 < n_kt) pf_wait_vm<NPEND>();
+    else pf_wait_vm<0>();
     __syncthreads();
-    if (kt + 1 < n_kt) cur = pf_load<D, V_F8>(kbase, kstride, vbase, vrow_stride, kt + 1, Lk);
+    // the stage of tile kt+2 was last read in tile kt-1: every wave is past it
+    if constexpr (V_F8) {
+      if (kt + 1 < n_kt) vload(kt + 1);
+    }
+    if (kt + 2 < n_kt) {
+      const int st2 = kst == 0 ? 2 : kst - 1;
+      pf_dma<D, V_F8>(krs, vrs, kvo, vvo, (uint32_t)(kt + 2) * ktile_bytes, (uint32_t)(kt + 2) * (PF_BN * 2), kdst(st2), vdst(st2));
+    }
+    const int cur = kst;
+    kst = kst == PF_NST - 1 ? 0 : kst + 1;
     const int kfirst = kt * PF_BN;
     if (kfirst >= wave_kend) continue;  // every key of this tile is masked for this wave
-    const uint8_t* sk = st;
-    const uint8_t* sv = st + L::KBYTES;
+    const uint8_t* sk = smem + G::K_OFF + cur * G::KBYTES;
+    const uint8_t* sv = smem + G::V_OFF + (V_F8 ? (kt & 1) : cur) * G::VBYTES;
 
     // ---- S^T = K Q^T (raw code products)
     float s[4][2][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const uint8_t* kp = sk + (kb * 16 + n) * L::KROW + g * QB;
-      const v4i ka = *reinterpret_cast<const v4i*>(kp);
+      const v4i ka = *reinterpret_cast<const v4i*>(sk + kb * 16 * D + kr0);
       v4i kb2 = v4i{0, 0, 0, 0};
-      if constexpr (QB == 32) kb2 = *reinterpret_cast<const v4i*>(kp + 16);
+      if constexpr (QB == 32) kb2 = *reinterpret_cast<const v4i*>(sk + kb * 16 * D + kr1);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if constexpr (QK_I8) {
@@ -230,10 +291,17 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
         }
       }
     }
+    // V^T operands of this tile, read while the softmax runs
+    v8h vop[D / 16][2];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      vop[db][0] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr0);
+      vop[db][1] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr1);
+    }
 
     float fold;
     if constexpr (QK_I8)
-      fold = base_fold * a.k_scale[((long)b * a.hkv + hk) * a.nblk_k + (kt * PF_BN) / 128];
+      fold = base_fold * k_sc_blk[kt >> 1];
     else
       fold = base_fold * k_sc_head;
 
@@ -314,12 +382,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const v8h vop = *reinterpret_cast<const v8h*>(sv + (db * 16 + n) * L::VROW + (ks * 32 + 8 * g) * 2);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk[qb][ks], oacc[db][qb], 0, 0, 0);
-      }
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db][ks], pk[qb][ks], oacc[db][qb], 0, 0, 0);
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
@@ -337,9 +403,16 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       const int d0 = db * 16 + 4 * g;
-      uint32_t w0 = f32_to_h16(oacc[db][qb][0] * inv, O_BF16) | (f32_to_h16(oacc[db][qb][1] * inv, O_BF16) << 16);
-      uint32_t w1 = f32_to_h16(oacc[db][qb][2] * inv, O_BF16) | (f32_to_h16(oacc[db][qb][3] * inv, O_BF16) << 16);
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + obase + d0) = u32x2{w0, w1};
+      const v4f o4 = oacc[db][qb] * inv;
+      u32x2 w;
+      if constexpr (O_BF16) {  // hardware round-to-nearest-even
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{o4[0], o4[1]}, v2bf));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{o4[2], o4[3]}, v2bf));
+      } else {
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{o4[0], o4[1]}, v2h));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{o4[2], o4[3]}, v2h));
+      }
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + obase + d0) = w;
     }
     if (a.lse && g == 0)
       a.lse[(long)h * a.total_q + q0 + row] = any ? (m_ref[qb] + __log2f(l)) * PF_LN2 : -INFINITY;
@@ -349,11 +422,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
 template <int D, bool I8, bool F8>
 static bool launch_t(const PrefillArgs& a, bool o_bf16, int tiles, hipStream_t s) {
   dim3 grid((unsigned)(a.batch * a.hq), (unsigned)tiles);
-  const size_t lds = 2 * PfLds<D>::STAGE;
   if (o_bf16)
-    hipLaunchKernelGGL((k_prefill<D, I8, F8, true>), grid, dim3(PF_THREADS), lds, s, a);
+    hipLaunchKernelGGL((k_prefill<D, I8, F8, true>), grid, dim3(PF_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_prefill<D, I8, F8, false>), grid, dim3(PF_THREADS), lds, s, a);
+    hipLaunchKernelGGL((k_prefill<D, I8, F8, false>), grid, dim3(PF_THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
 

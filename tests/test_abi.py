@@ -99,6 +99,7 @@ def test_prefill_validation():
     assert _prefill(sc=float("inf")) == -1
     assert _prefill(cq=None) == -1
     assert _prefill(vs=None) == -1 and "v_scale" in _err()
+    assert _prefill(mk=1 << 21, hkv=8, hq=8) == -2 and "2 GiB" in _err()   # 32-bit tile offsets
 
 
 def _decode(**kw):
