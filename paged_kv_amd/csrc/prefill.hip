@@ -118,9 +118,21 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int h = __builtin_amdgcn_readfirstlane(blockIdx.x % a.hq);
-  const int b = __builtin_amdgcn_readfirstlane(blockIdx.x / a.hq);
-  const int tile = gridDim.y - 1 - blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8),
+  // each with its own L2.  Re-index so that the workgroups one XCD runs
+  // together are consecutive query tiles of the same (sequence, head): they
+  // stream the same K/V tiles, which the XCD's L2 then serves once.  The
+  // map is a bijection of the grid when gridDim.x is a multiple of 8.
+  int bh = blockIdx.x, ty = blockIdx.y;
+  if ((gridDim.x & 7) == 0) {
+    const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+    const int j = lin >> 3;
+    bh = (lin & 7) + 8 * (j / gridDim.y);
+    ty = j % gridDim.y;
+  }
+  const int h = __builtin_amdgcn_readfirstlane(bh % a.hq);
+  const int b = __builtin_amdgcn_readfirstlane(bh / a.hq);
+  const int tile = gridDim.y - 1 - ty;
   const int q0 = clampi(a.cu_q[b], 0, a.total_q), q1 = clampi(a.cu_q[b + 1], q0, a.total_q);
   const int k0 = clampi(a.cu_k[b], 0, a.total_k), k1 = clampi(a.cu_k[b + 1], k0, a.total_k);
   // lengths beyond the host-given maxima would address past the padded V^T
