@@ -2,14 +2,19 @@
 // decode over paged_kv_indptr / paged_kv_indices / paged_kv_last_page_len;
 // aiter's paged fp8 flash_attn_with_kvcache with per-head descales).
 //
-// Split phase: one workgroup (4 waves) per (sequence, chunk of DEC_CHUNK_TOKENS
-// cached tokens); wave w handles kv heads w, w+4, ...  For each pair of
-// 16-token page blocks:
-//   K rows (NHD, one 128-byte row per token and kv head) are read straight
-//   into the A operand of S^T = K Q^T (bf16 16x16x32 MFMA, fp8 -> bf16 exact);
-//   the q heads of the group are the 16 columns (unused columns are zero);
-//   V is widened to fp16 and written transposed into a per-wave LDS tile in
-//   the token order of the P^T operand, then O^T += V^T P^T (fp16 MFMA).
+// Split phase: one workgroup per (sequence, chunk of DEC_CHUNK_TOKENS cached
+// tokens, group of 4 kv heads); each wave owns one kv head and runs its own
+// pipeline (no workgroup barriers).  Per step of 32 tokens (two 16-token
+// blocks, each inside one page since page sizes are multiples of 16):
+//   K rows (NHD: 128 bytes per token and kv head) are loaded one step ahead
+//   straight into the A operand of S^T = K Q^T (bf16 16x16x32 MFMA, fp8 ->
+//   bf16 exact); the G q heads of the group are the MFMA columns;
+//   V rows are copied one step ahead by direct loads into a per-wave LDS
+//   stage (fp8, rows XOR-swizzled in 16-byte chunks) and read back with the
+//   transposing 8-bit LDS read, which hands each lane the 8 tokens of one d
+//   that the PV A operand needs; widened to fp16 (exact), O^T += V^T P^T.
+//   Online softmax keeps a lagging reference max (rescale only when a score
+//   exceeds it by more than 2^8).
 // Each chunk writes its normalized partial O and its log2-sum-exp to the
 // caller's workspace; the merge kernel combines the chunks of a sequence.
 #include "kcommon.h"
@@ -18,27 +23,44 @@
 namespace attnq {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* dec_lds_t;
 
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_D = 128;
 constexpr int DEC_CHUNK_TOKENS = 512;
-constexpr int DEC_VROW = 32 * 2 + 16;  // bytes per LDS V^T row: 32 tokens fp16 + pad
+constexpr int DEC_BLKS = DEC_CHUNK_TOKENS / 16;    // 16-token blocks per chunk (one table lane each)
+static_assert(DEC_BLKS <= 64, "the block table lives in one VGPR");
+constexpr int DEC_STEP = 32;                      // tokens per step
+constexpr int DEC_VST = 2;                        // V stages per wave
+constexpr int DEC_VTILE = DEC_STEP * DEC_D;       // bytes of one fp8 V stage
 constexpr float DEC_LN2 = 0.69314718055994530942f;
+constexpr float DEC_REF_SLACK = 8.0f;             // log2 headroom before a rescale
 
-struct PairRegs {
-  uint4 k[2][2];  // [block][half]: 32 fp8 K bytes of token n, d in [32g, 32g+32)
-  uint4 v[2][2];  // same for V
-};
+// 16-byte chunk position of chunk c in V tile row t (bank-conflict-free
+// transposed reads: the 8 rows one 16-lane group reads land in 8 distinct
+// (row parity, chunk) bank groups)
+ATTNQ_DEV int dec_vsw(int t) { return ((t >> 1) + 2 * (t >> 4)) & 7; }
 
-__global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_split(const DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[4][DEC_D * DEC_VROW];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int N>
+ATTNQ_DEV void dec_wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt[3:0]; expcnt, lgkmcnt: no wait
+}
+
+__global__ __launch_bounds__(DEC_THREADS, 3) void k_decode_split(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[4][DEC_VST][DEC_VTILE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int chunk = blockIdx.x, b = blockIdx.y;
+  const int hk = blockIdx.z * 4 + wave;
+  if (hk >= a.hkv) return;
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
   const int npg = p1 - p0;
   const int ps = a.page_size;
@@ -46,177 +68,264 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_split(const DecodeArg
   const int t_begin = chunk * DEC_CHUNK_TOKENS;
   if (t_begin >= kv_len) return;
   const int t_end = min(kv_len, t_begin + DEC_CHUNK_TOKENS);
-  const int nblk = (t_end - t_begin + 15) / 16;  // 16-token blocks in this chunk
+  const int nblk = (t_end - t_begin + 15) / 16;        // 16-token blocks (<= DEC_BLKS)
+  const int vb_last = t_end - (t_begin + 16 * (nblk - 1));  // valid tokens of the last block
+  const int nsteps = (nblk + 1) / 2;
   const int G = a.hq / a.hkv;
-  uint8_t* sv = s_v[wave];
+  const long row_bytes = (long)a.hkv * DEC_D;          // bytes between consecutive slots of a page
 
-  for (int hk = wave; hk < a.hkv; hk += 4) {
-    // Q^T operand: lane (n, g) holds q head hk*G + n, d in [32g + 8j, 32g + 8j + 8) for MFMA j
-    v8bf qop[4];
-    {
-      const bool have = n < G;
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)b * a.hq + hk * G + n) * DEC_D + 32 * g;
+  // byte offset of 16-token block i of the chunk (lane i; blocks past the
+  // end repeat the last valid block so every address stays inside the cache)
+  long boff;
+  {
+    const int i = min(lane, nblk - 1);
+    const int tb = t_begin + 16 * i;
+    const int page = clampi(a.kv_indices[p0 + tb / ps], 0, a.num_pages - 1);
+    boff = ((long)page * ps + tb % ps) * row_bytes + (long)hk * DEC_D;
+  }
+  const uint32_t boff_lo = (uint32_t)boff, boff_hi = (uint32_t)(boff >> 32);
+  auto blk_off = [&](int i) -> long {  // wave-uniform
+    const uint32_t lo = __builtin_amdgcn_readlane(boff_lo, i), hi = __builtin_amdgcn_readlane(boff_hi, i);
+    return (long)(((uint64_t)hi << 32) | lo);
+  };
+  auto blk_valid = [&](int i) { return i < nblk - 1 ? 16 : vb_last; };  // for i >= nblk - 1: the last block
+
+  // Q^T operand: lane (n, g) holds q head hk*G + n, d in [32g + 8m, 32g + 8m + 8) for MFMA m
+  v8bf qop[4];
+  {
+    const bool have = n < G;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)b * a.hq + hk * G + n) * DEC_D + 32 * g;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 w = have ? *reinterpret_cast<const uint4*>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
-        qop[j] = __builtin_bit_cast(v8bf, w);
-      }
+    for (int m = 0; m < 4; ++m) {
+      const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 8 * m) : u32x4{0u, 0u, 0u, 0u};
+      qop[m] = __builtin_bit_cast(v8bf, w);
     }
-    const float kfold = a.sm_scale_log2 * a.k_scale[hk];
-    const float vsc = a.v_scale[hk];
-    v4f oacc[DEC_D / 16];
-#pragma unroll
-    for (int db = 0; db < DEC_D / 16; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+  }
+  const float kfold = a.sm_scale_log2 * a.k_scale[hk];
+  const float vsc = a.v_scale[hk];
 
-    auto load_pair = [&](int pair, PairRegs& r) {
+  // K of one step: [block][half], 32 bytes of token n (clamped into the block), d in [32g, 32g+32)
+  struct KRegs { u32x4 k[2][2]; };
+  const uint32_t k_lane = (uint32_t)(n * row_bytes + 32 * g);
+  auto load_k = [&](int st, KRegs& r) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = t_begin + (2 * pair + j) * 16 + n;  // token of this lane
-        r.k[j][0] = r.k[j][1] = r.v[j][0] = r.v[j][1] = make_uint4(0, 0, 0, 0);
-        if (t < t_end) {
-          int page = a.kv_indices[p0 + t / ps];
-          page = clampi(page, 0, a.num_pages - 1);
-          const long off = (((long)page * ps + t % ps) * a.hkv + hk) * DEC_D + 32 * g;
-          r.k[j][0] = *reinterpret_cast<const uint4*>(a.k_cache + off);
-          r.k[j][1] = *reinterpret_cast<const uint4*>(a.k_cache + off + 16);
-          r.v[j][0] = *reinterpret_cast<const uint4*>(a.v_cache + off);
-          r.v[j][1] = *reinterpret_cast<const uint4*>(a.v_cache + off + 16);
-        }
-      }
-    };
+    for (int j = 0; j < 2; ++j) {
+      const int i = min(2 * st + j, DEC_BLKS - 1);
+      const uint8_t* base = a.k_cache + blk_off(i);
+      const int vb = blk_valid(i);
+      const uint32_t off = vb == 16 ? k_lane : (uint32_t)(min(n, vb - 1) * row_bytes + 32 * g);
+      r.k[j][0] = *reinterpret_cast<const u32x4*>(base + off);
+      r.k[j][1] = *reinterpret_cast<const u32x4*>(base + off + 16);
+    }
+  };
+  // V of one step -> LDS stage: direct load i (0..3) fills tile rows 8i..8i+7
+  // (token rows of the step), lane L holds 16-byte chunk L%8 ^ swizzle of row 8i + L/8
+  uint8_t* vst0 = s_v[wave][0];
+  uint32_t v_lane[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v_lane[i] = (uint32_t)(((i & 1) * 8 + (lane >> 3)) * row_bytes + (((lane & 7) ^ dec_vsw(8 * i + (lane >> 3))) << 4));
+  auto load_v = [&](int st, int stage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bi = min(2 * st + (i >> 1), DEC_BLKS - 1);
+      const int vb = blk_valid(bi);
+      uint32_t off = v_lane[i];
+      if (vb < 16)  // rows past the end re-read the block's last valid token
+        off = (uint32_t)(min((i & 1) * 8 + (lane >> 3), vb - 1) * row_bytes +
+                         (((lane & 7) ^ dec_vsw(8 * i + (lane >> 3))) << 4));
+      // descriptor over the 16 slots of this block (wave-uniform 64-bit base)
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.v_cache + blk_off(bi)), (short)0, (int)(16 * row_bytes), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (dec_lds_t)(vst0 + stage * DEC_VTILE + i * 1024), 16, off, 0, 0, 0);
+    }
+  };
 
-    const int npairs = (nblk + 1) / 2;
-    PairRegs cur, nxt;
-    load_pair(0, cur);
-    for (int pair = 0; pair < npairs; ++pair) {
-      if (pair + 1 < npairs) load_pair(pair + 1, nxt);
-      // ---- S^T = K Q^T for the two 16-token blocks
-      float s[2][4];
+  // transposed-read row of this lane: k-slot 8g + e of the PV operand is token
+  // 16*(e/4) + 4g + e%4 (the S^T accumulator order); lane k of a 16-lane group
+  // supplies token slot e = k/2, bytes 8*(k%2) of the d chunk
+  const int tr_row = 16 * ((n >> 1) >> 2) + 4 * g + ((n >> 1) & 3);
+  const int tr_sw = dec_vsw(tr_row);
+  // LDS byte address (stage 0) of this lane's transposed read of d block db
+  uint32_t tra[DEC_D / 16];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-        uint32_t w[8] = {cur.k[j][0].x, cur.k[j][0].y, cur.k[j][0].z, cur.k[j][0].w,
-                         cur.k[j][1].x, cur.k[j][1].y, cur.k[j][1].z, cur.k[j][1].w};
+  for (int db = 0; db < DEC_D / 16; ++db)
+    tra[db] = (uint32_t)(uintptr_t)(dec_lds_t)(vst0 + tr_row * DEC_D + 8 * (n & 1) + ((db ^ tr_sw) << 4));
+
+  v4f oacc[DEC_D / 16];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // 8 fp8 codes (2 dwords) -> 8 bf16
-          v2bf c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * m], 1.0f, false);
-          v2bf c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * m], 1.0f, true);
-          v2bf c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * m + 1], 1.0f, false);
-          v2bf c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * m + 1], 1.0f, true);
-          v8bf kop = v8bf{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[m], acc, 0, 0, 0);
-        }
-        // lane (n, g) holds S^T[token 4g + r of block j][q head n]
+  for (int db = 0; db < DEC_D / 16; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;
+  const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
+
+  // one step on K registers kc while step st+1 is fetched into kn.  The
+  // fetch is unconditional (the last step re-reads its own, cached, rows) so
+  // that every step issues the same eight loads and the wait counts below are
+  // exact.
+  auto step = [&](auto stage_c, int st, const KRegs& kc, KRegs& kn) {
+    constexpr int STAGE = decltype(stage_c)::value;  // == st % 2
+    const bool more = st + 1 < nsteps;
+    const int nx = more ? st + 1 : st;
+    load_k(nx, kn);
+    load_v(nx, STAGE ^ 1);
+    // ---- S^T = K Q^T for the two 16-token blocks
+    float s[2][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t_begin + (2 * pair + j) * 16 + 4 * g + r;
-          s[j][r] = t < t_end ? acc[r] * kfold : -INFINITY;
-        }
+    for (int j = 0; j < 2; ++j) {
+      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w0 = kc.k[j][m >> 1][2 * (m & 1)], w1 = kc.k[j][m >> 1][2 * (m & 1) + 1];
+        const v2bf c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        const v2bf c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        const v2bf c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        const v2bf c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+        const v8bf kop = v8bf{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[m], acc, 0, 0, 0);
       }
-      // ---- V^T staging: token n of block j -> LDS column pos = 8*(n/4) + 4j + n%4
+      // lane (n, g) holds S^T[token 16j + 4g + r of the step][q head n]
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = t_begin + (2 * pair + j) * 16 + n;
-        const bool valid = t < t_end;
-        const int col = 8 * (n / 4) + 4 * j + (n % 4);
-        uint32_t w[8] = {cur.v[j][0].x, cur.v[j][0].y, cur.v[j][0].z, cur.v[j][0].w,
-                         cur.v[j][1].x, cur.v[j][1].y, cur.v[j][1].z, cur.v[j][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(valid ? w[e] : 0u, 1.0f, false);
-          v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(valid ? w[e] : 0u, 1.0f, true);
-          const int d0 = 32 * g + 4 * e;
-          _Float16* base = reinterpret_cast<_Float16*>(sv + col * 2);
-          base[(d0 + 0) * (DEC_VROW / 2)] = lo[0];
-          base[(d0 + 1) * (DEC_VROW / 2)] = lo[1];
-          base[(d0 + 2) * (DEC_VROW / 2)] = hi[0];
-          base[(d0 + 3) * (DEC_VROW / 2)] = hi[1];
-        }
-      }
-      // ---- online softmax over the 32 tokens of this pair
-      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      v8h pk;
-      float rs = 0.f;
+      for (int r = 0; r < 4; ++r) s[j][r] = acc[r] * kfold;
+    }
+    if (!more) {  // the last step may run past the chunk's end
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[j][r] - m_use);
-          rs += p;
-          pk[4 * j + r] = (_Float16)p;
-        }
-      l_run = l_run * alpha + rs;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int db = 0; db < DEC_D / 16; ++db) {
-        oacc[db] *= alpha;
-        const uint4 vv = *reinterpret_cast<const uint4*>(sv + (db * 16 + n) * DEC_VROW + 16 * g);
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, vv), pk, oacc[db], 0, 0, 0);
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (pair + 1 < npairs) cur = nxt;
+        for (int r = 0; r < 4; ++r)
+          if (t_begin + st * DEC_STEP + 16 * j + 4 * g + r >= t_end) s[j][r] = -INFINITY;
     }
-    // ---- partial results: O_c = O / l (times the V descale, fp8 -> fp16 was exact),
-    //      lse_c = m + log2(l) in log2 units
-    float l = l_run;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (n < G) {
-      const int qh = hk * G + n;
-      const long row = ((long)b * a.hq + qh) * a.n_chunks + chunk;
-      const float inv = l > 0.f ? vsc / l : 0.f;
+    // ---- online softmax against a lagging reference max
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (__ballot(mx > m_ref + DEC_REF_SLACK)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DEC_D / 16; ++db) {
-        float4 o4 = make_float4(oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv);
-        *reinterpret_cast<float4*>(a.ws_o + row * DEC_D + db * 16 + 4 * g) = o4;
-      }
-      if (g == 0) a.ws_lse[row] = l > 0.f ? m_run + __log2f(l) : -INFINITY;
+      for (int db = 0; db < DEC_D / 16; ++db) oacc[db] *= alpha;
     }
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+    v8h pk;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const v2h ph = __builtin_convertvector(
+            (v4f{__builtin_amdgcn_exp2f(s[j][r] - m_use), __builtin_amdgcn_exp2f(s[j][r + 1] - m_use), 0.f, 0.f}).xy, v2h);
+        pk[4 * j + r] = ph[0];
+        pk[4 * j + r + 1] = ph[1];
+        l_run = __builtin_amdgcn_fdot2(ph, ones, l_run, false);
+      }
+    // ---- O^T += V^T P^T; the step's V stage has landed (only step st+1's
+    // eight loads may still be in flight)
+    dec_wait_vm<8>();
+    // the eight transposed reads as one block (the compiler would otherwise
+    // drain every in-flight direct load before each of them)
+    v2i raw[DEC_D / 16];
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(raw[4]), "=&v"(raw[5]),
+          "=&v"(raw[6]), "=&v"(raw[7])
+        : "v"(tra[0]), "v"(tra[1]), "v"(tra[2]), "v"(tra[3]), "v"(tra[4]), "v"(tra[5]), "v"(tra[6]),
+          "v"(tra[7]), "i"(STAGE * DEC_VTILE)
+        : "memory");
+#pragma unroll
+    for (int db = 0; db < DEC_D / 16; ++db) {
+      const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][0], 1.0f, false);
+      const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][0], 1.0f, true);
+      const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][1], 1.0f, false);
+      const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][1], 1.0f, true);
+      const v8h vop = v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[db], 0, 0, 0);
+    }
+  };
+
+  KRegs ka, kb;
+  load_k(0, ka);
+  load_v(0, 0);
+  for (int st = 0; st < nsteps; st += 2) {  // two register sets, no copies
+    step(std::integral_constant<int, 0>{}, st, ka, kb);
+    if (st + 1 < nsteps) step(std::integral_constant<int, 1>{}, st + 1, kb, ka);
+  }
+  dec_wait_vm<0>();  // no direct load may outlive the workgroup's LDS
+  // ---- partial results: O_c = O / l (times the V descale, fp8 -> fp16 was exact),
+  //      lse_c = m + log2(l) in log2 units
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (n < G) {
+    const int qh = hk * G + n;
+    const long row = ((long)b * a.hq + qh) * a.n_chunks + chunk;
+    const float inv = l > 0.f ? vsc / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < DEC_D / 16; ++db)
+      *reinterpret_cast<v4f*>(a.ws_o + row * DEC_D + db * 16 + 4 * g) = oacc[db] * inv;
+    if (g == 0) a.ws_lse[row] = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
   }
 }
 
-// Merge: O = sum_c 2^(lse_c - lse) O_c, lse = log2 sum_c 2^lse_c.  One
-// 32-lane group per (sequence, q head), four d values per lane.
-constexpr int MERGE_THREADS = 128;
+// Merge: O = sum_c 2^(lse_c - lse) O_c, lse = log2 sum_c 2^lse_c.  One wave
+// per (sequence, q head): lane c holds chunk c's lse (64 chunks per pass), the
+// weights come from a wave max / sum, and each lane accumulates two d values
+// over the chunks with eight independent loads in flight.
+constexpr int MERGE_THREADS = 256;
+
+ATTNQ_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
 __global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(const DecodeArgs a) {
-  const int row = blockIdx.x * (MERGE_THREADS / 32) + threadIdx.x / 32;  // b * hq + qh
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6);  // b * hq + qh
   if (row >= a.batch * a.hq) return;
   const int b = row / a.hq;
-  const int d0 = (threadIdx.x % 32) * 4;
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
   const int npg = p1 - p0;
   const int kv_len = npg > 0 ? (npg - 1) * a.page_size + clampi(a.kv_last[b], 0, a.page_size) : 0;
   const int nc = min(a.n_chunks, (kv_len + DEC_CHUNK_TOKENS - 1) / DEC_CHUNK_TOKENS);
   const long row0 = (long)row * a.n_chunks;
   float m = -INFINITY;
-  for (int c = 0; c < nc; ++c) m = fmaxf(m, a.ws_lse[row0 + c]);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nc; c0 += 64)
+    m = fmaxf(m, wave_max(c0 + lane < nc ? a.ws_lse[row0 + c0 + lane] : -INFINITY));
   float tot = 0.f;
+  v2f acc = v2f{0.f, 0.f};
   if (m != -INFINITY) {
-    for (int c = 0; c < nc; ++c) {
-      const float lc = a.ws_lse[row0 + c];
-      if (lc == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(lc - m);
-      tot += w;
-      const float4 o4 = *reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * DEC_D + d0);
-      acc[0] += w * o4.x; acc[1] += w * o4.y; acc[2] += w * o4.z; acc[3] += w * o4.w;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const float lc = c0 + lane < nc ? a.ws_lse[row0 + c0 + lane] : -INFINITY;
+      const float w = lc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lc - m);
+      tot += wave_sum(w);
+      const int cn = min(64, nc - c0);
+      const float* op = a.ws_o + (row0 + c0) * DEC_D + 2 * lane;
+      int c = 0;
+      for (; c + 8 <= cn; c += 8) {
+        v2f o8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o8[u] = *reinterpret_cast<const v2f*>(op + (long)(c + u) * DEC_D);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), c + u)) * o8[u];
+      }
+      for (; c < cn; ++c)
+        acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), c)) *
+               *reinterpret_cast<const v2f*>(op + (long)c * DEC_D);
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  uint32_t w0 = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
-  uint32_t w1 = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + (long)row * DEC_D + d0) = make_uint2(w0, w1);
-  if (a.lse && d0 == 0) a.lse[row] = tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
+  const v2bf ob = __builtin_convertvector(acc * inv, v2bf);
+  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.o) + (long)row * DEC_D + 2 * lane) = __builtin_bit_cast(uint32_t, ob);
+  if (a.lse && lane == 0) a.lse[row] = tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
 }
 
 int decode_chunk_pages(int page_size) { return DEC_CHUNK_TOKENS / page_size; }
@@ -233,10 +342,10 @@ size_t decode_workspace_bytes(int batch, int hq, int head_dim, int max_kv_len, i
 
 bool launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return true;
-  hipLaunchKernelGGL(k_decode_split, dim3(a.n_chunks, a.batch), dim3(DEC_THREADS), 0, s, a);
+  hipLaunchKernelGGL(k_decode_split, dim3(a.n_chunks, a.batch, (a.hkv + 3) / 4), dim3(DEC_THREADS), 0, s, a);
   if (hipGetLastError() != hipSuccess) return false;
   const int rows = a.batch * a.hq;
-  hipLaunchKernelGGL(k_decode_merge, dim3((rows + MERGE_THREADS / 32 - 1) / (MERGE_THREADS / 32)),
+  hipLaunchKernelGGL(k_decode_merge, dim3((rows + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64)),
                      dim3(MERGE_THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
