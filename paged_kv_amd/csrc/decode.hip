@@ -53,7 +53,7 @@ ATTNQ_DEV void dec_wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt[3:0]; expcnt, lgkmcnt: no wait
 }
 
-__global__ __launch_bounds__(DEC_THREADS, 3) void k_decode_split(const DecodeArgs a) {
+__global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_v[4][DEC_VST][DEC_VTILE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,32 +90,34 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void k_decode_split(const DecodeArg
   };
   auto blk_valid = [&](int i) { return i < nblk - 1 ? 16 : vb_last; };  // for i >= nblk - 1: the last block
 
-  // Q^T operand: lane (n, g) holds q head hk*G + n, d in [32g + 8m, 32g + 8m + 8) for MFMA m
+  // Q^T operand: lane (n, g) holds q head hk*G + n, d in [64(m/2) + 16g + 8(m%2), +8)
+  // for MFMA m (the K operand below uses the same d order)
   v8bf qop[4];
   {
     const bool have = n < G;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)b * a.hq + hk * G + n) * DEC_D + 32 * g;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)b * a.hq + hk * G + n) * DEC_D + 16 * g;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 8 * m) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 64 * (m >> 1) + 8 * (m & 1)) : u32x4{0u, 0u, 0u, 0u};
       qop[m] = __builtin_bit_cast(v8bf, w);
     }
   }
   const float kfold = a.sm_scale_log2 * a.k_scale[hk];
   const float vsc = a.v_scale[hk];
 
-  // K of one step: [block][half], 32 bytes of token n (clamped into the block), d in [32g, 32g+32)
+  // K of one step: [block][half], bytes [16g, 16g+16) and [64+16g, 64+16g+16) of
+  // token n (clamped into the block): each load reads 64 contiguous bytes per row
   struct KRegs { u32x4 k[2][2]; };
-  const uint32_t k_lane = (uint32_t)(n * row_bytes + 32 * g);
+  const uint32_t k_lane = (uint32_t)(n * row_bytes + 16 * g);
   auto load_k = [&](int st, KRegs& r) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = min(2 * st + j, DEC_BLKS - 1);
       const uint8_t* base = a.k_cache + blk_off(i);
       const int vb = blk_valid(i);
-      const uint32_t off = vb == 16 ? k_lane : (uint32_t)(min(n, vb - 1) * row_bytes + 32 * g);
+      const uint32_t off = vb == 16 ? k_lane : (uint32_t)(min(n, vb - 1) * row_bytes + 16 * g);
       r.k[j][0] = *reinterpret_cast<const u32x4*>(base + off);
-      r.k[j][1] = *reinterpret_cast<const u32x4*>(base + off + 16);
+      r.k[j][1] = *reinterpret_cast<const u32x4*>(base + off + 64);
     }
   };
   // V of one step -> LDS stage: direct load i (0..3) fills tile rows 8i..8i+7
@@ -254,10 +256,15 @@ __global__ __launch_bounds__(DEC_THREADS, 3) void k_decode_split(const DecodeArg
   KRegs ka, kb;
   load_k(0, ka);
   load_v(0, 0);
-  for (int st = 0; st < nsteps; st += 2) {  // two register sets, no copies
+  // two register sets, no copies; the loop body always runs both halves (a
+  // conditional second half would let the compiler assume a prefetch into kb
+  // still in flight at the top of the loop and wait for it there)
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
     step(std::integral_constant<int, 0>{}, st, ka, kb);
-    if (st + 1 < nsteps) step(std::integral_constant<int, 1>{}, st + 1, kb, ka);
+    step(std::integral_constant<int, 1>{}, st + 1, kb, ka);
   }
+  if (st < nsteps) step(std::integral_constant<int, 0>{}, st, ka, kb);
   dec_wait_vm<0>();  // no direct load may outlive the workgroup's LDS
   // ---- partial results: O_c = O / l (times the V descale, fp8 -> fp16 was exact),
   //      lse_c = m + log2(l) in log2 units
