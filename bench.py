@@ -15,7 +15,12 @@ long fp8 prefill with RoPE + paged append (TFLOP/s), the sparse MLA decode
 ``roofline``: the prefill kernel alone, timed with HIP events on the stream
 it is launched on, against the MFMA peak of its two contractions (int8 QK at
 5.0 POP/s, fp16 PV at 2.5 PFLOP/s: 2 / (1/5000 + 1/2500) = 3333 TFLOP/s for
-equal flop counts).  ``cpu_baseline``: the fp64 oracle on a bounded sample
+equal flop counts).  ``traffic``: HBM-side bytes of one launch from two
+rocprofv3 counter runs of ``bench.py --traffic-probe`` (FETCH_SIZE, then
+WRITE_SIZE), each scaled by what the same counter reads for a device copy of
+known size; ``bench.py --summarize-traffic`` stores them under profiles/
+with a hash of the kernel sources, and the figure is reported only while
+that hash matches.  ``cpu_baseline``: the fp64 oracle on a bounded sample
 of the same workload, on the host cores.
 """
 from __future__ import annotations
@@ -38,6 +43,11 @@ PEAK_FP8 = 5000.0        # TFLOP/s dense
 PEAK_I8 = 5000.0         # TOP/s dense
 PEAK_F16 = 2500.0        # TFLOP/s dense
 PEAK_HBM = 8000.0        # GB/s
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_prefill_sage_varlen.md")
+TRAFFIC_SOURCES = ("paged_kv_amd/csrc/prefill.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")
+CALIB_BYTES = 256 << 20  # device-to-device copy used to scale the counters
 
 
 def log(*a):
@@ -173,6 +183,98 @@ def bench_config4(iters):
             "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12}
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_probe():
+    """One calibration copy of CALIB_BYTES and one headline prefill launch
+    (run under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)."""
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import SagePrefill
+    from tests.parity import to_dev
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    x = gen.config2()
+    p = SagePrefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
+                    int(x["seqlens"].max()), x["sm_scale"], causal=True)
+    p.quantize()
+    torch.cuda.synchronize()
+    p.attend()
+    torch.cuda.synchronize()
+    log("[bench] traffic probe done")
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return list(csv.DictReader(open(f[0])))
+
+
+def summarize_traffic(fetch_dir, write_dir, fetch_cmd, write_cmd):
+    """Turn the two counter runs into profiles/traffic_k_prefill_sage_varlen.md."""
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        pf = [float(r["Counter_Value"]) for r in rows if "k_prefill" in r["Kernel_Name"]]
+        if not copies or len(pf) != 1:
+            raise SystemExit(f"{name}: expected copy dispatches and one k_prefill dispatch, got {len(copies)}, {len(pf)}")
+        calib = max(copies)  # KiB for the CALIB_BYTES copy
+        factor = (CALIB_BYTES / 1024.0) / calib
+        out[name] = {"kernel_kib": pf[0], "copy_kib": calib, "factor": factor, "bytes": pf[0] * factor * 1024.0}
+    traffic = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    h = kernel_source_hash()
+    lines = [
+        "# HBM-side traffic of one k_prefill launch (int8 QK / fp16 PV, sage varlen workload)",
+        "",
+        "Workload: B=8, lengths U{512..4096} (seed 1002), causal, Hq=32, Hkv=8, D=128; one launch of",
+        "`attn_prefill_varlen` after `attn_quant_qk` / `attn_quant_v_permute` (bench.py --traffic-probe).",
+        "",
+        "Commands (from the repository root on the GPU host, `cd /tmp && export TMPDIR=/tmp` first):",
+        "",
+        f"    {fetch_cmd}",
+        f"    {write_cmd}",
+        "",
+        "Calibration: a device-to-device copy of 256 MiB (__amd_rocclr_copyBuffer) moves 262144 KiB each way;",
+        "each counter is scaled by 262144 / (its reading for that copy).",
+        "",
+        "| counter | k_prefill (KiB) | 256 MiB copy (KiB) | factor | k_prefill bytes |",
+        "|---|---|---|---|---|",
+    ]
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[name]
+        lines.append(f"| {name} | {o['kernel_kib']:.0f} | {o['copy_kib']:.0f} | {o['factor']:.4f} | {o['bytes']:.4g} |")
+    lines += ["", f"traffic_bytes_per_launch: {traffic:.6g}", f"kernel_source_hash: {h}", ""]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps({"traffic_bytes": traffic, "hash": h, **out}))
+
+
+def stored_traffic():
+    """Bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(l.split(": ", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch", "kernel_source_hash")))
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(x, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the config-2 workload: whole
     heads of the first sequence, added until the time budget is spent."""
@@ -213,7 +315,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extra", default="c3,c5,c4", help="comma list of extra workloads (c3,c4,c5) or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run the calibration copy and one prefill launch (for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "FETCH_CMD", "WRITE_CMD"),
+                    help="write the traffic summary under profiles/ from two counter runs")
     a = ap.parse_args()
+    if a.summarize_traffic:
+        summarize_traffic(*a.summarize_traffic)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -223,6 +332,9 @@ def main():
     torch.cuda.set_device(0)
     import paged_kv_amd
     paged_kv_amd.lib()
+    if a.traffic_probe:
+        traffic_probe()
+        return
 
     log("[bench] config2 (headline)")
     r2 = bench_config2(a.steps, a.warmup)
@@ -257,7 +369,7 @@ def main():
                    "step_flop": r2["flops"]},
         "pct_fp8_peak": 100 * value / PEAK_FP8,
         "roofline": {"bound": "mfma", "achieved": k_tflops, "peak": peak_mixed, "unit": "TFLOP/s",
-                     "frac": k_tflops / peak_mixed, "traffic": None,
+                     "frac": k_tflops / peak_mixed, "traffic": stored_traffic(),
                      "kernel": "k_prefill<128, int8 QK, fp16 V>",
                      "per_launch_flop": r2["flops"], "avg_launch_ms": r2["kernel_ms"]},
         "cpu_baseline": cpu,
