@@ -79,6 +79,20 @@ ATTNQ_DEV void e4m3x4_to_f16x4_scaled(uint32_t w, uint32_t& lo, uint32_t& hi) {
   hi = ((h >> 1) & 0x3f803f80u) | (h & 0x80008000u);
 }
 
+// x / s correctly rounded, from r = 1/s (itself correctly rounded) in three
+// operations: q0 = x r, e = x - q0 s (exact through the fused multiply-add),
+// q = q0 + e r (Markstein's correction), with the sign of x kept for -0.
+// Equal to the IEEE quotient whenever it is a normal number; where the
+// quotient is subnormal it may differ in its last bits only, which no int8
+// or e4m3fn code can see.  Valid for s >= 1e-30 (1/s finite); callers use the
+// plain division below that.
+ATTNQ_DEV float quot_by_recip(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+constexpr float QUOT_MIN_SCALE = 1e-30f;
+
 ATTNQ_DEV int32_t int8_encode(float v) {
   float r = __builtin_rintf(v);
   r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);

@@ -4,9 +4,10 @@
 //
 // Sources: PaddleNLP "Sage Attention Support Varlen" (varlen quant qk and
 // quant_transpose_permute v kernels); aiter "[Triton] FP8 with FA v3 API"
-// (fp8 q/k/v with per-head descales).  Arithmetic: one IEEE fp32 division
-// x / scale per element (never a reciprocal multiply), so that codes are
-// bit-identical to a plain definition of the quantizer.
+// (fp8 q/k/v with per-head descales).  Arithmetic: the codes are those of the
+// correctly rounded fp32 quotient x / scale, so that they are bit-identical
+// to a plain definition of the quantizer; the quotient is formed from one
+// reciprocal per scale and a fused-multiply-add correction (quot_by_recip).
 #include "kcommon.h"
 #include "launch.h"
 
@@ -67,66 +68,85 @@ __global__ void k_finalize_scale(const float* __restrict__ amax_in, float* scale
   scales[h] = (a == 0.0f) ? 1.0f : a / qmax;
 }
 
-// codes = e4m3fn(x / descale[head]), 8 elements per work item.
-__global__ __launch_bounds__(256) void k_quant_fp8(const uint16_t* __restrict__ x, long n_chunks,
-                                                   int heads, int dim, int is_bf16,
-                                                   const float* __restrict__ descale,
-                                                   uint8_t* __restrict__ codes) {
-  const int cpr_head = dim / 8;
-  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks;
-       i += (long)gridDim.x * blockDim.x) {
-    int h = (int)((i / cpr_head) % heads);
-    float d = descale[h];
-    uint4 v = reinterpret_cast<const uint4*>(x)[i];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t out[2];
+// codes = e4m3fn(x / descale[head]).  x is [rows, heads, dim]; a thread owns
+// one 16-byte chunk column of the row (so one head, one descale and its
+// reciprocal) for FP8_ROWS consecutive rows, whose loads are all in flight
+// before the first is encoded.
+constexpr int FP8_THREADS = 256;
+constexpr int FP8_ROWS = 16;
+
+template <bool BF16, int CPRH>
+__global__ __launch_bounds__(FP8_THREADS) void k_quant_fp8(const uint16_t* __restrict__ x, int rows, int heads,
+                                                           const float* __restrict__ descale,
+                                                           uint8_t* __restrict__ codes) {
+  const int cr = heads * CPRH;  // 16-byte chunks per row
+  const int cc = blockIdx.y * FP8_THREADS + threadIdx.x;
+  if (cc >= cr) return;
+  const float d = descale[cc / CPRH];
+  const float r = 1.0f / d;
+  const int r0 = blockIdx.x * FP8_ROWS;
+  const int nr = min(FP8_ROWS, rows - r0);
+  const u32x4* src = reinterpret_cast<const u32x4*>(x) + (long)r0 * cr + cc;
+  u32x4 v[FP8_ROWS];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      uint32_t c0 = e4m3fn_encode(h16_to_f32(w[2 * p] & 0xffffu, is_bf16) / d);
-      uint32_t c1 = e4m3fn_encode(h16_to_f32(w[2 * p] >> 16, is_bf16) / d);
-      uint32_t c2 = e4m3fn_encode(h16_to_f32(w[2 * p + 1] & 0xffffu, is_bf16) / d);
-      uint32_t c3 = e4m3fn_encode(h16_to_f32(w[2 * p + 1] >> 16, is_bf16) / d);
-      out[p] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  for (int k = 0; k < FP8_ROWS; ++k) v[k] = src[(long)min(k, nr - 1) * cr];
+  u32x2* dst = reinterpret_cast<u32x2*>(codes) + (long)r0 * cr + cc;
+#pragma unroll
+  for (int k = 0; k < FP8_ROWS; ++k) {
+    if (k >= nr) continue;
+    uint32_t c[8];
+    if (d >= QUOT_MIN_SCALE) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        c[e] = e4m3fn_encode(quot_by_recip(h16_to_f32(e & 1 ? v[k][e >> 1] >> 16 : v[k][e >> 1] & 0xffffu, BF16), d, r));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        c[e] = e4m3fn_encode(h16_to_f32(e & 1 ? v[k][e >> 1] >> 16 : v[k][e >> 1] & 0xffffu, BF16) / d);
     }
-    reinterpret_cast<uint2*>(codes)[i] = make_uint2(out[0], out[1]);
+    dst[(long)k * cr] = u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                              c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
   }
 }
 
 // ---------------------------------------------------------------- int8 per block
-// One workgroup per (block j, head h, sequence b): the block's rows are
-// loaded once into registers, reduced to amax, then quantized.
+// One workgroup per (block j, head h, sequence b): the block's rows (at most
+// 128) are loaded into registers in one go (rows past the sequence end
+// re-read its last row and are left out of the max), reduced to amax, then
+// encoded.
 constexpr int I8_THREADS = 256;
-constexpr int I8_MAX_CHUNKS = 8;  // 128 rows * 128 dim / 8 / 256 threads
+constexpr int I8_BLOCK = 128;
 
+template <bool BF16, int DIM>
 __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int dim,
-    int block_tokens, int nblk, int is_bf16, int total_tokens, int8_t* __restrict__ codes,
-    float* __restrict__ scales) {
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int nblk,
+    int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales) {
+  constexpr int CPR = DIM / 8;                          // 16-byte chunks per row
+  constexpr int NCH = I8_BLOCK * CPR / I8_THREADS;      // chunks per thread
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
-  const int r0 = s0 + j * block_tokens;
+  const int r0 = s0 + j * I8_BLOCK;
   float* sc_out = scales + ((long)b * heads + h) * nblk + j;
   if (r0 >= s1) {
     if (threadIdx.x == 0) *sc_out = 0.0f;
     return;
   }
-  const int nrows = min(block_tokens, s1 - r0);
-  const int cpr = dim / 8;
-  const int nchunks = nrows * cpr;
-  uint4 v[I8_MAX_CHUNKS];
+  const int nrows = min(I8_BLOCK, s1 - r0);
+  u32x4 v[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = threadIdx.x + k * I8_THREADS;
+    const int row = min(c / CPR, nrows - 1), col = (c % CPR) * 8;
+    v[k] = *reinterpret_cast<const u32x4*>(x + ((long)(r0 + row) * heads + h) * DIM + col);
+  }
   float m = 0.0f;
 #pragma unroll
-  for (int k = 0; k < I8_MAX_CHUNKS; ++k) {
-    int c = threadIdx.x + k * I8_THREADS;
-    v[k] = make_uint4(0, 0, 0, 0);
-    if (c < nchunks) {
-      int row = c / cpr, col = (c % cpr) * 8;
-      v[k] = *reinterpret_cast<const uint4*>(x + ((long)(r0 + row) * heads + h) * dim + col);
-      uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+  for (int k = 0; k < NCH; ++k) {
+    if ((threadIdx.x + k * I8_THREADS) / CPR < nrows) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m = fmaxf(m, fabsf(h16_to_f32(w[e] & 0xffffu, is_bf16)));
-        m = fmaxf(m, fabsf(h16_to_f32(w[e] >> 16, is_bf16)));
+        m = fmaxf(m, fabsf(h16_to_f32(v[k][e] & 0xffffu, BF16)));
+        m = fmaxf(m, fabsf(h16_to_f32(v[k][e] >> 16, BF16)));
       }
     }
   }
@@ -139,25 +159,27 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
   for (int w = 1; w < I8_THREADS / 64; ++w) amax = fmaxf(amax, s_red[w]);
   const float scale = (amax == 0.0f) ? 1.0f : amax / 127.0f;
   if (threadIdx.x == 0) *sc_out = scale;
+  const float rs = 1.0f / scale;
+  auto encode_all = [&](auto fast_c) {
+    constexpr bool FAST = decltype(fast_c)::value;
 #pragma unroll
-  for (int k = 0; k < I8_MAX_CHUNKS; ++k) {
-    int c = threadIdx.x + k * I8_THREADS;
-    if (c < nchunks) {
-      int row = c / cpr, col = (c % cpr) * 8;
-      uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-      uint32_t out[2];
+    for (int k = 0; k < NCH; ++k) {
+      const int c = threadIdx.x + k * I8_THREADS;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      if (row < nrows) {
+        uint32_t q[8];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        uint32_t q0 = (uint32_t)int8_encode(h16_to_f32(w[2 * p] & 0xffffu, is_bf16) / scale) & 0xffu;
-        uint32_t q1 = (uint32_t)int8_encode(h16_to_f32(w[2 * p] >> 16, is_bf16) / scale) & 0xffu;
-        uint32_t q2 = (uint32_t)int8_encode(h16_to_f32(w[2 * p + 1] & 0xffffu, is_bf16) / scale) & 0xffu;
-        uint32_t q3 = (uint32_t)int8_encode(h16_to_f32(w[2 * p + 1] >> 16, is_bf16) / scale) & 0xffu;
-        out[p] = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+        for (int e = 0; e < 8; ++e) {
+          const float xv = h16_to_f32(e & 1 ? v[k][e >> 1] >> 16 : v[k][e >> 1] & 0xffffu, BF16);
+          q[e] = (uint32_t)int8_encode(FAST ? quot_by_recip(xv, scale, rs) : xv / scale) & 0xffu;
+        }
+        *reinterpret_cast<u32x2*>(codes + ((long)(r0 + row) * heads + h) * DIM + col) =
+            u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24), q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
       }
-      *reinterpret_cast<uint2*>(codes + ((long)(r0 + row) * heads + h) * dim + col) =
-          make_uint2(out[0], out[1]);
     }
-  }
+  };
+  if (scale >= QUOT_MIN_SCALE) encode_all(std::true_type{});  // uniform
+  else encode_all(std::false_type{});
 }
 
 // ---------------------------------------------------------------- V transpose / permute
@@ -191,6 +213,8 @@ __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
   }
   __syncthreads();
   const float ds = fp8 ? descale[h] : 1.0f;
+  const float rds = 1.0f / ds;
+  const bool fast = ds >= QUOT_MIN_SCALE;  // uniform
   const long row_base = ((long)b * heads + h) * dim;
   for (int it = threadIdx.x; it < dim * (VP_TILE / 8); it += VP_THREADS) {
     int d = it / (VP_TILE / 8), p0 = (it % (VP_TILE / 8)) * 8;
@@ -201,8 +225,13 @@ __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
     long o = (row_base + d) * s_pad + t0 + p0;
     if (fp8) {
       uint32_t c[8];
+      if (fast) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) c[s] = e4m3fn_encode(h16_to_f32(e16[s], is_bf16) / ds);
+        for (int s = 0; s < 8; ++s) c[s] = e4m3fn_encode(quot_by_recip(h16_to_f32(e16[s], is_bf16), ds, rds));
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) c[s] = e4m3fn_encode(h16_to_f32(e16[s], is_bf16) / ds);
+      }
       *reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + o) =
           make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
@@ -241,12 +270,19 @@ bool launch_finalize_scale(const float* amax_in, float* scales, int heads, float
 
 bool launch_quant_fp8(const void* x, long elems, int heads, int dim, bool is_bf16,
                       const float* descale, void* codes, hipStream_t s) {
-  long n_chunks = elems / 8;
-  if (n_chunks <= 0) return true;
-  long want = (n_chunks + 255) / 256;
-  int grid = (int)(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(k_quant_fp8, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                     n_chunks, heads, dim, (int)is_bf16, descale, static_cast<uint8_t*>(codes));
+  const long rows = elems / ((long)heads * dim);
+  if (rows <= 0) return true;
+  const int cr = heads * dim / 8;
+  const dim3 grid((unsigned)((rows + FP8_ROWS - 1) / FP8_ROWS), (unsigned)((cr + FP8_THREADS - 1) / FP8_THREADS));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint8_t* cp = static_cast<uint8_t*>(codes);
+  if (dim == 128) {
+    if (is_bf16) hipLaunchKernelGGL((k_quant_fp8<true, 16>), grid, dim3(FP8_THREADS), 0, s, xp, (int)rows, heads, descale, cp);
+    else hipLaunchKernelGGL((k_quant_fp8<false, 16>), grid, dim3(FP8_THREADS), 0, s, xp, (int)rows, heads, descale, cp);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((k_quant_fp8<true, 8>), grid, dim3(FP8_THREADS), 0, s, xp, (int)rows, heads, descale, cp);
+    else hipLaunchKernelGGL((k_quant_fp8<false, 8>), grid, dim3(FP8_THREADS), 0, s, xp, (int)rows, heads, descale, cp);
+  }
   return ok(hipGetLastError());
 }
 
@@ -254,9 +290,17 @@ bool launch_quant_int8_block(const void* x, const int32_t* cu, int batch, int he
                              int block_tokens, int nblk, bool is_bf16, int total_tokens,
                              void* codes, float* scales, hipStream_t s) {
   if (batch <= 0 || nblk <= 0) return true;
-  hipLaunchKernelGGL(k_quant_int8_block, dim3(nblk, heads, batch), dim3(I8_THREADS), 0, s,
-                     static_cast<const uint16_t*>(x), cu, heads, dim, block_tokens, nblk,
-                     (int)is_bf16, total_tokens, static_cast<int8_t*>(codes), scales);
+  if (block_tokens != I8_BLOCK) return false;
+  const dim3 grid(nblk, heads, batch);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  int8_t* cp = static_cast<int8_t*>(codes);
+  if (dim == 128) {
+    if (is_bf16) hipLaunchKernelGGL((k_quant_int8_block<true, 128>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales);
+    else hipLaunchKernelGGL((k_quant_int8_block<false, 128>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((k_quant_int8_block<true, 64>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales);
+    else hipLaunchKernelGGL((k_quant_int8_block<false, 64>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales);
+  }
   return ok(hipGetLastError());
 }
 
