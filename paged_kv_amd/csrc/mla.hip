@@ -57,7 +57,7 @@ struct MlaStage {
 constexpr int MLA_NBUF = 2;  // staging buffers: step st computes, step st + 1 is staged
 struct MlaLds {
   MlaStage buf[MLA_NBUF];
-  float xs[4][4][8][64];          // partial scores of the 4 channel tiles of each head block
+  v4f xs[4][2][4][64];            // partial scores [head block][16-token block][channel tile][lane]
   int row_idx[MLA_SPLIT_TOKENS];  // cache row of each selected index, -1 if unused
 };
 
@@ -197,9 +197,15 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
   }
   for (int st = 0; st < nsteps; ++st) {
     MlaStage& B = L.buf[st % MLA_NBUF];
-    float (*xs)[4][8][64] = L.xs;
+    v4f (*xs)[2][4][64] = L.xs;
     // ---- partial S^T of this wave's tile, lane (n, g): tokens 16j + 4g + r, head n
     float sp[2][4];
+    // this lane's tokens' scales of tile t (used by QK and by P)
+    float sc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[j][r] = B.scale[(16 * j + 4 * g + r) * 4 + t];
     if (wave_active) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qn[m], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sp[j][r] = B.scale[(16 * j + 4 * g + r) * 4 + t] * acc[r];
+        for (int r = 0; r < 4; ++r) sp[j][r] = sc[j][r] * acc[r];
         if (t == 3) {
           v4f racc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -221,8 +227,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sp[j][r] += racc[r];
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xs[hb][t][4 * j + r][lane] = sp[j][r];
+        xs[hb][j][t][lane] = v4f{sp[j][0], sp[j][1], sp[j][2], sp[j][3]};
       }
     }
     __syncthreads();  // scores exchanged; the PV of step st - 1 is done everywhere
@@ -233,15 +238,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
       __syncthreads();
       continue;
     }
+    // used indices of the step: bit e of `mine` is token 4g + e of the step
+    const uint64_t used = __ballot(lane < MLA_STEP && L.row_idx[st * MLA_STEP + (lane & (MLA_STEP - 1))] >= 0);
+    const uint32_t mine = (uint32_t)(used >> (4 * g));
     float s[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const v4f tot = (xs[hb][j][0][lane] + xs[hb][j][1][lane]) + (xs[hb][j][2][lane] + xs[hb][j][3][lane]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float tot = (xs[hb][0][4 * j + r][lane] + xs[hb][1][4 * j + r][lane]) +
-                          (xs[hb][2][4 * j + r][lane] + xs[hb][3][4 * j + r][lane]);
-        s[j][r] = L.row_idx[st * MLA_STEP + 16 * j + 4 * g + r] >= 0 ? tot * a.sm_scale_log2 : -INFINITY;
-      }
+      for (int r = 0; r < 4; ++r) s[j][r] = (mine >> (16 * j + r)) & 1u ? tot[r] * a.sm_scale_log2 : -INFINITY;
+    }
 
     // ---- softmax against a lagging reference max (the four waves of a
     // head block compute identical values); exact path when a step would
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
     v8h pk;
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl)
-      pk[sl] = (_Float16)(p[sl] * B.scale[((sl / 4) * 16 + 4 * g + (sl % 4)) * 4 + t]);
+      pk[sl] = (_Float16)(p[sl] * sc[sl / 4][sl % 4]);
     // address lane (g, 4k + q) names token (4g + k) (+16), channels 4q..4q+3 of the d-block
     const int tr_row = 4 * g + (n >> 2), tr_col = 4 * (n & 3);
 #pragma unroll
