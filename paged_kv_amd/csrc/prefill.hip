@@ -5,10 +5,10 @@
 // prefill; aiter's fp8 flash_attn_func with q/k/v descales; PaddleNLP's Sage
 // attention over a varlen batch with per-block int8 Q/K).
 //
-// Work split: one workgroup (4 waves) per (sequence, q head, 128-query tile);
-// the grid's y index runs over query tiles from the end of the sequence
-// (the tiles with the most visible keys start first).  Each wave owns 32
-// queries and streams 64-key tiles staged in LDS (double-buffered).
+// Work split: one workgroup (4 waves) per (sequence, q head, 128-query tile); the grid's y
+// index runs over query tiles from the end of the sequence (the tiles with
+// the most visible keys start first).  Each wave owns 32 queries and streams
+// 64-key tiles staged in LDS by direct loads (three-stage ring).
 //
 // Per key tile and wave:
 //   S^T = K Q^T          fp8 16x16x128 MFMA (or two int8 16x16x64), fp32/i32 acc;
@@ -37,8 +37,16 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int PF_THREADS = 256;
-constexpr int PF_BM = 128;  // queries per workgroup (4 waves x 32)
+// Workgroup shape: each wave owns 32 queries; 4 waves (128 queries), two
+// workgroups per CU.  (8 waves / 256 queries halve the K/V tile traffic but
+// leave one workgroup per CU, whose barriers nothing covers: measured slower
+// on the varlen workload, about even on the long one.)
+template <int D>
+struct PfShape {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BM = WAVES * 32;  // queries per workgroup
+};
 constexpr int PF_BN = 64;   // keys per tile
 constexpr int PF_NST = 3;   // LDS stages of the DMA ring (two tiles in flight)
 constexpr float PF_LN2 = 0.69314718055994530942f;
@@ -56,10 +64,13 @@ struct PfGeo {
   static constexpr int K_CH = D / 16;                  // chunks per K row (codes)
   static constexpr int KBYTES = PF_BN * D;             // one K tile
   static constexpr int VBYTES = D * PF_BN * 2;         // one V^T tile (fp16, 128-byte rows)
-  static constexpr int NKD = KBYTES / 1024 / 4;        // K direct loads per wave per tile
-  static constexpr int NVD = V_F8 ? 0 : VBYTES / 1024 / 4;  // V^T direct loads per wave per tile
+  static constexpr int WAVES = PfShape<D>::WAVES;
+  static constexpr int THREADS = PfShape<D>::THREADS;
+  static constexpr int NKD = KBYTES / 1024 / WAVES;                // K direct loads per wave per tile
+  static constexpr int NVD = V_F8 ? 0 : VBYTES / 1024 / WAVES;     // V^T direct loads per wave per tile
+  static_assert(NKD >= 1 && (V_F8 || NVD >= 1), "every wave takes a share of each tile");
   static constexpr int NV_ST = V_F8 ? 2 : PF_NST;      // V^T stages (fp8 V is widened through registers)
-  static constexpr int VC = V_F8 ? D * PF_BN / 16 / PF_THREADS : 0;  // fp8 V^T u32x4 per thread
+  static constexpr int VC = V_F8 ? D * PF_BN / 16 / THREADS : 0;     // fp8 V^T u32x4 per thread
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = PF_NST * KBYTES;
   static constexpr int LDS = V_OFF + NV_ST * VBYTES;
@@ -112,7 +123,7 @@ ATTNQ_DEV void pf_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, co
 constexpr float PF_TILE_SUM_MAX = 16384.0f;
 
 template <int D, bool QK_I8, bool V_F8, bool O_BF16>
-__global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) {
+__global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const PrefillArgs a) {
   using G = PfGeo<D, V_F8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   const int lane = threadIdx.x & 63;
@@ -138,12 +149,13 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   // lengths beyond the host-given maxima would address past the padded V^T
   // rows and the scale arrays: clamp (a broken precondition, not a fault)
   const int Lq = min(q1 - q0, a.max_q), Lk = min(k1 - k0, a.max_k);
-  const int qs = tile * PF_BM;
+  constexpr int BM = PfShape<D>::BM;
+  const int qs = tile * BM;
   if (qs >= Lq) return;
   const int hk = __builtin_amdgcn_readfirstlane(h / (a.hq / a.hkv));
   const int off = Lk - Lq;  // bottom-right causal alignment
   int kend = Lk;
-  if (a.causal) kend = min(Lk, qs + PF_BM + off);
+  if (a.causal) kend = min(Lk, qs + BM + off);
   const int n_kt = kend > 0 ? (kend + PF_BN - 1) / PF_BN : 0;
   const int wq0 = qs + wave * 32;  // first query of this wave
   // keys visible to this wave's last query end here (wave-uniform)
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   }
 
   float q_sc;
-  if constexpr (QK_I8) q_sc = a.q_scale[((long)b * a.hq + h) * a.nblk_q + tile];
+  if constexpr (QK_I8) q_sc = a.q_scale[((long)b * a.hq + h) * a.nblk_q + (wq0 >> 7)];  // 128-query block
   else q_sc = a.q_scale[h];
   const float k_sc_head = QK_I8 ? 0.0f : a.k_scale[hk];
   // int8: one scale per 128-key block, read through the scalar cache (the
@@ -208,14 +220,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
   auto vload = [&](int t) {
     static_for<0, G::VC>([&](auto ci) {
       constexpr int c = decltype(ci)::value;
-      const int idx = threadIdx.x + c * PF_THREADS;
+      const int idx = threadIdx.x + c * G::THREADS;
       vreg[c] = *reinterpret_cast<const u32x4*>(vbase + (long)t * PF_BN + (idx >> 2) * vrow + (idx & 3) * 16);
     });
   };
   auto vstore = [&](int stage) {
     static_for<0, G::VC>([&](auto ci) {
       constexpr int c = decltype(ci)::value;
-      const int idx = threadIdx.x + c * PF_THREADS;
+      const int idx = threadIdx.x + c * G::THREADS;
       const int r = idx >> 2, j = idx & 3;
       u32x4 lo, hi;
       pf_widen_fp8(vreg[c], lo, hi);
@@ -432,25 +444,25 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill(const PrefillArgs a) 
 }
 
 template <int D, bool I8, bool F8>
-static bool launch_t(const PrefillArgs& a, bool o_bf16, int tiles, hipStream_t s) {
+static bool launch_t(const PrefillArgs& a, bool o_bf16, int max_seqlen_q, hipStream_t s) {
+  const int tiles = (max_seqlen_q + PfShape<D>::BM - 1) / PfShape<D>::BM;
   dim3 grid((unsigned)(a.batch * a.hq), (unsigned)tiles);
   if (o_bf16)
-    hipLaunchKernelGGL((k_prefill<D, I8, F8, true>), grid, dim3(PF_THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<D, I8, F8, true>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_prefill<D, I8, F8, false>), grid, dim3(PF_THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<D, I8, F8, false>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
 
 bool launch_prefill(const PrefillArgs& a, int head_dim, bool qk_int8, bool v_fp8, bool o_bf16,
                     int max_seqlen_q, hipStream_t s) {
-  const int tiles = (max_seqlen_q + PF_BM - 1) / PF_BM;
-  if (tiles <= 0 || a.batch <= 0) return true;
+  if (max_seqlen_q <= 0 || a.batch <= 0) return true;
   if (head_dim == 128) {
-    if (qk_int8) return v_fp8 ? launch_t<128, true, true>(a, o_bf16, tiles, s) : launch_t<128, true, false>(a, o_bf16, tiles, s);
-    return v_fp8 ? launch_t<128, false, true>(a, o_bf16, tiles, s) : launch_t<128, false, false>(a, o_bf16, tiles, s);
+    if (qk_int8) return v_fp8 ? launch_t<128, true, true>(a, o_bf16, max_seqlen_q, s) : launch_t<128, true, false>(a, o_bf16, max_seqlen_q, s);
+    return v_fp8 ? launch_t<128, false, true>(a, o_bf16, max_seqlen_q, s) : launch_t<128, false, false>(a, o_bf16, max_seqlen_q, s);
   }
-  if (qk_int8) return v_fp8 ? launch_t<64, true, true>(a, o_bf16, tiles, s) : launch_t<64, true, false>(a, o_bf16, tiles, s);
-  return v_fp8 ? launch_t<64, false, true>(a, o_bf16, tiles, s) : launch_t<64, false, false>(a, o_bf16, tiles, s);
+  if (qk_int8) return v_fp8 ? launch_t<64, true, true>(a, o_bf16, max_seqlen_q, s) : launch_t<64, true, false>(a, o_bf16, max_seqlen_q, s);
+  return v_fp8 ? launch_t<64, false, true>(a, o_bf16, max_seqlen_q, s) : launch_t<64, false, false>(a, o_bf16, max_seqlen_q, s);
 }
 
 }  // namespace attnq
