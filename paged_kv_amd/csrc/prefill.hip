@@ -289,7 +289,10 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     const uint8_t* sk = smem + G::K_OFF + cur * G::KBYTES;
     const uint8_t* sv = smem + G::V_OFF + (V_F8 ? (kt & 1) : cur) * G::VBYTES;
 
-    // ---- S^T = K Q^T (raw code products)
+    // ---- S^T = K Q^T (raw code products).  The MFMA blocks run at raised
+    // wave priority: when both waves of a SIMD are ready, the one entering its
+    // matrix section issues first and the other's softmax fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
     float s[4][2][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -315,6 +318,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // V^T operands of this tile, read while the softmax runs
     v8h vop[D / 16][2];
 #pragma unroll
@@ -403,6 +407,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     l_run[1] += lt[1];
 
     // ---- O^T += V^T P^T
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -410,6 +415,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db][ks], pk[qb][ks], oacc[db][qb], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
