@@ -139,14 +139,18 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  *     qk_dtype INT8 with scale_mode INT8_PER_BLOCK (q_scale [B, Hq, ceil(max_seqlen_q/128)],
  *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk).
  *   v_perm: attn_quant_v_permute's output for the keys, [B, Hkv, D, round_up(max_seqlen_k,128)];
- *     v_dtype FP8E4M3 (v_scale [Hkv]) or FP16 / BF16 (v_scale ignored).
+ *     v_dtype FP8E4M3 (v_scale [Hkv]) or FP16 (v_scale ignored).  The padding
+ *     past each sequence's keys must hold finite values (attn_quant_v_permute
+ *     writes zeros there): it meets p = 0 in the PV product.
  *   logit(i, j) = sm_scale * Dequant(q_i) . Dequant(k_j); q head h reads kv head
  *   h / (Hq/Hkv).  causal: key j visible to query i iff j <= i + L_k - L_q
  *   (bottom-right aligned).
  *   o [total_q, num_q_heads, head_dim], o_dtype BF16 or FP16.
  *   lse optional fp32 [num_q_heads, total_q], natural log; rows with no visible
  *   key get o = 0 and lse = -inf.
- *   Supported: head_dim 64 or 128; (FP8, FP8 V) or (INT8, FP16/BF16 V).
+ *   Supported: head_dim 64 or 128; either Q/K mode with either V type;
+ *   max_seqlen_k * num_kv_heads * head_dim < 2^31 (tiles are addressed with
+ *   32-bit offsets inside one sequence), else ATTNQ_EUNSUPPORTED.
  */
 int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk_dtype,
                         int v_dtype, const float* q_scale, const float* k_scale,
