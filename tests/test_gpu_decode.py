@@ -40,10 +40,18 @@ def test_decode_small(ps):
     _check(x, 1 / math.sqrt(128), label=f"ps={ps}")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (12, 4)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (12, 4), (6, 3), (10, 5), (16, 16)])
 def test_decode_group_sizes(hq, hkv):
     x = gen.paged_decode_inputs(52, [700, 64, 2000], hq, hkv, 128, page_size=16)
     _check(x, 0.09, label=f"{hq}/{hkv}")
+
+
+@pytest.mark.parametrize("ps", [48, 1024])
+def test_decode_page_sizes_and_chunk_edges(ps):
+    # pages that do not divide the 512-token chunk (48) or hold two chunks (1024);
+    # lengths on and next to chunk and page boundaries
+    x = gen.paged_decode_inputs(54, [511, 512, 513, 1537, 47, 2048], 16, 4, 128, page_size=ps)
+    _check(x, 1 / math.sqrt(128), label=f"ps={ps}")
 
 
 def test_decode_page_permutation_bit_identical():
