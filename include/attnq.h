@@ -53,7 +53,8 @@ typedef enum { ATTNQ_BF16 = 0, ATTNQ_FP16 = 1, ATTNQ_FP8E4M3 = 2, ATTNQ_INT8 = 3
 typedef enum {
   ATTNQ_Q_FP8_PER_HEAD = 0,   /* fp8 e4m3fn codes, one fp32 descale per head */
   ATTNQ_Q_INT8_PER_BLOCK = 1, /* int8 codes, one fp32 scale per (seq, head, 128-token block) */
-  ATTNQ_Q_NONE = 2            /* unquantized 16-bit data */
+  ATTNQ_Q_NONE = 2,           /* unquantized 16-bit data */
+  ATTNQ_Q_FP8_PER_HEAD_WIDE = 3 /* fp8 e4m3fn codes as above, each stored as its exact fp16 value */
 } attnq_qmode;
 
 int attnq_abi_version(void);
@@ -94,6 +95,10 @@ int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int bat
  *          prefill kernel's PV operand reads a 32-token group).
  *   mode   FP8_PER_HEAD: enc = e4m3fn code as in attn_quant_qk, 1 byte/element,
  *          v_scales fp32 [num_kv_heads] receives the descales;
+ *          FP8_PER_HEAD_WIDE: the same codes and descales, each code stored as
+ *          its value in fp16 (exact for every finite e4m3fn code), 2 bytes/element:
+ *          the prefill then stages V with no widening step (pass v_dtype FP16
+ *          and the descales as v_scale);
  *          NONE: enc = the unchanged 16-bit value, v_scales ignored.
  *   amax_in optional, as in attn_quant_qk.
  */
@@ -139,7 +144,8 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  *     qk_dtype INT8 with scale_mode INT8_PER_BLOCK (q_scale [B, Hq, ceil(max_seqlen_q/128)],
  *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk).
  *   v_perm: attn_quant_v_permute's output for the keys, [B, Hkv, D, round_up(max_seqlen_k,128)];
- *     v_dtype FP8E4M3 (v_scale [Hkv]) or FP16 (v_scale ignored).  The padding
+ *     v_dtype FP8E4M3 (v_scale [Hkv] required) or FP16 (v_scale optional: when
+ *     given, V = value * v_scale[kv head], as for FP8_PER_HEAD_WIDE).  The padding
  *     past each sequence's keys must hold finite values (attn_quant_v_permute
  *     writes zeros there): it meets p = 0 in the PV product.
  *   logit(i, j) = sm_scale * Dequant(q_i) . Dequant(k_j); q head h reads kv head

@@ -112,15 +112,16 @@ int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, 
   REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   REQUIRE(num_kv_heads > 0 && num_kv_heads <= 1024, ATTNQ_EINVAL, "num_kv_heads must be in [1, 1024]");
   REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0, ATTNQ_EINVAL, "sizes must be >= 0");
-  REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_NONE, ATTNQ_EINVAL,
-          "mode must be FP8_PER_HEAD or NONE");
+  REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_FP8_PER_HEAD_WIDE || mode == ATTNQ_Q_NONE, ATTNQ_EINVAL,
+          "mode must be FP8_PER_HEAD, FP8_PER_HEAD_WIDE or NONE");
   REQUIRE_PTR(cu_seqlens, 4);
   REQUIRE_OPT_PTR(amax_in, 4);
   const int s_pad = round_up(max_seqlen, 128);
   if (batch > 0 && s_pad > 0) REQUIRE_PTR(v_out, 16);
   if (total_tokens > 0) REQUIRE_PTR(v, 16);
   const bool bf = v_dtype == ATTNQ_BF16;
-  const bool fp8 = mode == ATTNQ_Q_FP8_PER_HEAD;
+  const bool wide = mode == ATTNQ_Q_FP8_PER_HEAD_WIDE;
+  const bool fp8 = mode == ATTNQ_Q_FP8_PER_HEAD || wide;
   if (fp8) {
     REQUIRE_PTR(v_scales, 4);
     if (!amax_in) {
@@ -131,7 +132,7 @@ int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, 
     LAUNCHED(attnq::launch_finalize_scale(amax_in, v_scales, num_kv_heads, 448.0f, stream));
   }
   LAUNCHED(attnq::launch_v_permute(v, cu_seqlens, batch, num_kv_heads, head_dim, s_pad, bf,
-                                   total_tokens, fp8, fp8 ? v_scales : nullptr, v_out, stream));
+                                   total_tokens, fp8, wide, fp8 ? v_scales : nullptr, v_out, stream));
   return ok();
 }
 
@@ -207,6 +208,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   REQUIRE_PTR(q_scale, 4);
   REQUIRE_PTR(k_scale, 4);
   if (v_dtype == ATTNQ_FP8E4M3) REQUIRE_PTR(v_scale, 4);
+  else REQUIRE_OPT_PTR(v_scale, 4);
   if (total_q > 0) {
     REQUIRE_PTR(q, 16);
     REQUIRE_PTR(o, 16);

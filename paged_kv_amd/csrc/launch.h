@@ -17,8 +17,8 @@ bool launch_quant_int8_block(const void* x, const int32_t* cu, int batch, int he
                              int block_tokens, int nblk, bool is_bf16, int total_tokens,
                              void* codes, float* scales, hipStream_t s);
 bool launch_v_permute(const void* v, const int32_t* cu, int batch, int heads, int dim, int s_pad,
-                      bool is_bf16, int total_tokens, bool fp8, const float* descale, void* out,
-                      hipStream_t s);
+                      bool is_bf16, int total_tokens, bool fp8, bool wide, const float* descale,
+                      void* out, hipStream_t s);
 
 bool rope_units_fit(int hq, int hkv, int dim);
 bool launch_append_rope(void* q, void* k, const void* v, bool is_bf16, const int32_t* cu,

@@ -419,7 +419,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
-  const float vsc = V_F8 ? a.v_scale[hk] : 1.0f;
+  // V descale: fp8 codes, or fp16 values that carry one (the widened codes)
+  const float vsc = a.v_scale ? a.v_scale[hk] : 1.0f;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float l = l_run[qb];

@@ -192,7 +192,7 @@ constexpr int VP_TILE = 64;
 
 __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu, int heads, int dim,
-    int s_pad, int is_bf16, int total_tokens, int fp8, const float* __restrict__ descale,
+    int s_pad, int is_bf16, int total_tokens, int fp8, int wide, const float* __restrict__ descale,
     void* __restrict__ out) {
   __shared__ uint16_t s_t[128][VP_TILE + 2];  // [d][token], padded rows
   const int t0 = blockIdx.x * VP_TILE, h = blockIdx.y, b = blockIdx.z;
@@ -232,9 +232,18 @@ __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
 #pragma unroll
         for (int s = 0; s < 8; ++s) c[s] = e4m3fn_encode(h16_to_f32(e16[s], is_bf16) / ds);
       }
-      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + o) =
-          make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+      const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      if (wide) {  // each code's value in fp16 (exact)
+        u32x4 h;
+        h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+        h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+        h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+        h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + o) = h;
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + o) = make_uint2(w0, w1);
+      }
     } else {
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) =
           make_uint4(e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
@@ -305,12 +314,12 @@ bool launch_quant_int8_block(const void* x, const int32_t* cu, int batch, int he
 }
 
 bool launch_v_permute(const void* v, const int32_t* cu, int batch, int heads, int dim, int s_pad,
-                      bool is_bf16, int total_tokens, bool fp8, const float* descale, void* out,
-                      hipStream_t s) {
+                      bool is_bf16, int total_tokens, bool fp8, bool wide, const float* descale,
+                      void* out, hipStream_t s) {
   if (batch <= 0 || s_pad <= 0) return true;
   hipLaunchKernelGGL(k_v_permute, dim3(s_pad / VP_TILE, heads, batch), dim3(VP_THREADS), 0, s,
                      static_cast<const uint16_t*>(v), cu, heads, dim, s_pad, (int)is_bf16,
-                     total_tokens, (int)fp8, descale, out);
+                     total_tokens, (int)fp8, (int)wide, descale, out);
   return ok(hipGetLastError());
 }
 

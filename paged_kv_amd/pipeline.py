@@ -29,10 +29,12 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 class Fp8Prefill:
     """fp8 per-head quantization of Q/K/V followed by the varlen prefill
-    (the aiter fp8 flash_attn_func flow over a ragged batch)."""
+    (the aiter fp8 flash_attn_func flow over a ragged batch).  With
+    wide_v (default) the permuted V holds each fp8 code's exact fp16 value,
+    which the prefill stages without a widening step."""
 
     def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True,
-                 out_dtype=torch.bfloat16, want_lse=False, amax=None):
+                 out_dtype=torch.bfloat16, want_lse=False, amax=None, wide_v=True):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
@@ -43,8 +45,9 @@ class Fp8Prefill:
         self.amax = amax  # optional (amax_q, amax_k, amax_v) from the append step
         self.qc = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         self.kc = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+        self.wide_v = bool(wide_v)
         self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_seqlen, 128)),
-                              dtype=torch.uint8, device=dev)
+                              dtype=torch.float16 if self.wide_v else torch.uint8, device=dev)
         self.qs = torch.empty(self.hq, dtype=torch.float32, device=dev)
         self.ks = torch.empty(self.hkv, dtype=torch.float32, device=dev)
         self.vs = torch.empty(self.hkv, dtype=torch.float32, device=dev)
@@ -59,10 +62,12 @@ class Fp8Prefill:
         A.attn_quant_qk(self.k, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d,
                         A.Q_FP8_PER_HEAD, 128, ak, self.kc, self.ks)
         A.attn_quant_v_permute(self.v, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
-                               self.d, A.Q_FP8_PER_HEAD, av, self.vp, self.vs)
+                               self.d, A.Q_FP8_PER_HEAD_WIDE if self.wide_v else A.Q_FP8_PER_HEAD,
+                               av, self.vp, self.vs)
 
     def attend(self):
-        A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3, A.FP8E4M3, self.qs, self.ks,
+        A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3,
+                              A.FP16 if self.wide_v else A.FP8E4M3, self.qs, self.ks,
                               self.vs, A.Q_FP8_PER_HEAD, self.cu, self.cu, self.b, self.max_seqlen,
                               self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
                               self.sm_scale, self.causal, self.o, _dtype_code(self.o), self.lse)

@@ -7,6 +7,7 @@ import pytest
 
 import gen
 from oracle.attention import dequant_fp8_per_head, dequant_int8_per_block, prefill_varlen
+from oracle.numerics import e4m3fn_decode, to_fp16
 from oracle.quant import quant_fp8_per_head, quant_int8_per_block, v_permute, as_f32
 from tests.parity import to_dev, from_dev_bits, dev_u8, decode_out, compare_outputs, compare_lse
 
@@ -15,19 +16,19 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def _fp8_flow(x, sm_scale, causal=True, lse=True):
+def _fp8_flow(x, sm_scale, causal=True, lse=True, wide_v=True):
     from paged_kv_amd.pipeline import Fp8Prefill
     cu = x["cu_seqlens"]
     mx = int(np.diff(cu).max()) if len(cu) > 1 else 0
     p = Fp8Prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(cu), mx, sm_scale,
-                   causal=causal, want_lse=lse)
+                   causal=causal, want_lse=lse, wide_v=wide_v)
     p.run()
     torch.cuda.synchronize()
     return p, mx
 
 
-def _check_fp8(x, sm_scale, causal=True, label=""):
-    p, mx = _fp8_flow(x, sm_scale, causal)
+def _check_fp8(x, sm_scale, causal=True, label="", wide_v=True):
+    p, mx = _fp8_flow(x, sm_scale, causal, wide_v=wide_v)
     cu = x["cu_seqlens"]
     qc, qs = quant_fp8_per_head(x["q"], "bf16")
     kc, ks = quant_fp8_per_head(x["k"], "bf16")
@@ -35,7 +36,10 @@ def _check_fp8(x, sm_scale, causal=True, label=""):
     vperm, _ = v_permute(x["v"], "bf16", cu, mx, fp8=True)
     # quantized inputs are bit-exact
     assert np.array_equal(dev_u8(p.qc), qc) and np.array_equal(dev_u8(p.kc), kc)
-    assert np.array_equal(dev_u8(p.vp), vperm)
+    if wide_v:  # each code stored as its exact fp16 value
+        assert np.array_equal(from_dev_bits(p.vp), to_fp16(e4m3fn_decode(vperm)).view(np.uint16))
+    else:
+        assert np.array_equal(dev_u8(p.vp), vperm)
     for a, b in ((p.qs, qs), (p.ks, ks), (p.vs, vs)):
         assert np.array_equal(a.cpu().numpy().view(np.uint32), b.view(np.uint32))
     ref = prefill_varlen(dequant_fp8_per_head(qc, qs), dequant_fp8_per_head(kc, ks),
@@ -54,11 +58,13 @@ def test_config1_fp8_varlen():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_ragged_edges(d, causal):
-    # empty, single-token, exactly one tile, one past a tile, long ragged
+@pytest.mark.parametrize("wide_v", [True, False])
+def test_fp8_ragged_edges(d, causal, wide_v):
+    # empty, single-token, exactly one tile, one past a tile, long ragged;
+    # V as fp8 codes and as their fp16 values
     lens = [1, 0, 128, 129, 64, 65, 300]
     x = gen.prefill_fp8_inputs(31, lens, 4, 2, d, outlier_p=0.001)
-    _check_fp8(x, 1 / math.sqrt(d), causal, f"ragged d={d} causal={causal}")
+    _check_fp8(x, 1 / math.sqrt(d), causal, f"ragged d={d} causal={causal} wide_v={wide_v}", wide_v)
 
 
 def test_fp8_gqa_8to1():
