@@ -40,6 +40,7 @@ struct PrefillArgs {
   void* o;
   float* lse;
   int batch, hq, hkv, s_pad, nblk_q, nblk_k, total_q, total_k, causal, max_q, max_k;
+  int tblk;               // query tiles per block of the workgroup order (set by launch_prefill)
   float sm_scale_log2;    // sm_scale * log2(e)
 };
 // qk_int8: int8 per-block Q/K (else fp8 per-head); v_fp8: fp8 V (else fp16 V)

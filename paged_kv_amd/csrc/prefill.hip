@@ -49,6 +49,7 @@ struct PfShape {
 };
 constexpr int PF_BN = 64;   // keys per tile
 constexpr int PF_NST = 3;   // LDS stages of the DMA ring (two tiles in flight)
+constexpr int PF_TBLK_WGS = 64;  // workgroups per K/V stream in one block of the work order
 constexpr float PF_LN2 = 0.69314718055994530942f;
 // buffer descriptor word 3 for untyped 32-bit accesses
 constexpr int PF_RSRC_W3 = 0x00020000;
@@ -91,6 +92,16 @@ ATTNQ_DEV void pf_wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// Workgroup barrier of the LDS ring.  This wave's LDS stores have completed
+// (lgkmcnt 0) and its direct loads were waited for explicitly above it.  A
+// __syncthreads() would add a release fence, which waits for every vector
+// memory operation, including the next tile's direct loads still in flight.
+ATTNQ_DEV void pf_barrier() {
+  // gfx9 s_waitcnt: lgkmcnt[11:8]=0, vmcnt[3:0]+[15:14] and expcnt[6:4] at maximum
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
 // 16 fp8 codes (one u32x4) -> 16 fp16 values (exact), two u32x4.
 ATTNQ_DEV void pf_widen_fp8(const u32x4 w, u32x4& lo, u32x4& hi) {
   lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false));
@@ -122,6 +133,41 @@ ATTNQ_DEV void pf_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, co
 // fp16, and O / l need no rescale.
 constexpr float PF_TILE_SUM_MAX = 16384.0f;
 
+// Work item (sequence b, q head h, query tile counted from the sequence end
+// ty) of linear workgroup id lin; ntiles query tiles per (sequence, head).
+// Workgroups are dealt round-robin to the 8 XCDs (id mod 8), each with its own
+// L2.  When the kv heads split evenly over the XCDs, XCD x takes the kv heads
+// hk = x (mod 8) and runs its share in blocks of tblk query tiles, the tiles
+// with the most keys first (so that no long workgroup starts late).  Inside a
+// block it goes stream by stream ((sequence, kv head)), then tile by tile,
+// the q heads of one kv head side by side: workgroups that run together read
+// the same K/V tiles, which the XCD's L2 then serves once.  Otherwise tiles
+// with the most keys go first over all (sequence, head) pairs.  Both maps are
+// bijections of [0, batch*hq*ntiles).
+ATTNQ_DEV void pf_work_item(const PrefillArgs& a, int ntiles, int lin, int& b, int& h, int& ty) {
+  if ((a.hkv & 7) == 0) {
+    const int grp = a.hq / a.hkv;
+    const int xcd = lin & 7, j = lin >> 3;
+    const int nstream = a.batch * (a.hkv >> 3);  // (sequence, kv head) streams of this XCD
+    const int tb = max(1, min(a.tblk, ntiles));
+    const int blk = j / (nstream * tb * grp);
+    const int t0 = blk * tb;
+    const int tl = min(tb, ntiles - t0);          // the last block may be short
+    const int r = j - blk * (nstream * tb * grp);
+    const int st = r / (tl * grp), r2 = r - st * (tl * grp);
+    const int t = r2 / grp;
+    b = st % a.batch;
+    h = (xcd + 8 * (st / a.batch)) * grp + (r2 - t * grp);
+    ty = t0 + t;
+  } else {
+    const int nbh = a.batch * a.hq;
+    const int bh = lin % nbh;
+    b = bh / a.hq;
+    h = bh - b * a.hq;
+    ty = lin / nbh;
+  }
+}
+
 template <int D, bool QK_I8, bool V_F8, bool O_BF16>
 __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const PrefillArgs a) {
   using G = PfGeo<D, V_F8>;
@@ -129,21 +175,11 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  // Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8),
-  // each with its own L2.  Re-index so that the workgroups one XCD runs
-  // together are consecutive query tiles of the same (sequence, head): they
-  // stream the same K/V tiles, which the XCD's L2 then serves once.  The
-  // map is a bijection of the grid when gridDim.x is a multiple of 8.
-  int bh = blockIdx.x, ty = blockIdx.y;
-  if ((gridDim.x & 7) == 0) {
-    const int lin = blockIdx.x + blockIdx.y * gridDim.x;
-    const int j = lin >> 3;
-    bh = (lin & 7) + 8 * (j / gridDim.y);
-    ty = j % gridDim.y;
-  }
-  const int h = __builtin_amdgcn_readfirstlane(bh % a.hq);
-  const int b = __builtin_amdgcn_readfirstlane(bh / a.hq);
-  const int tile = gridDim.y - 1 - ty;
+  int b, h, ty;
+  pf_work_item(a, (int)gridDim.x / (a.batch * a.hq), (int)blockIdx.x, b, h, ty);
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  const int tile = (int)gridDim.x / (a.batch * a.hq) - 1 - ty;
   const int q0 = clampi(a.cu_q[b], 0, a.total_q), q1 = clampi(a.cu_q[b + 1], q0, a.total_q);
   const int k0 = clampi(a.cu_k[b], 0, a.total_k), k1 = clampi(a.cu_k[b + 1], k0, a.total_k);
   // lengths beyond the host-given maxima would address past the padded V^T
@@ -176,6 +212,10 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     }
     lim[qb] = a.causal ? min(Lk, row + off + 1) : Lk;
   }
+  // Q has landed before the first tile load is issued.  Otherwise the
+  // compiler, unable to tell the Q loads from the tile loads in flight in the
+  // loop, drains the next tile's loads before every tile's first MFMA.
+  pf_wait_vm<0>();
 
   float q_sc;
   if constexpr (QK_I8) q_sc = a.q_scale[((long)b * a.hq + h) * a.nblk_q + (wq0 >> 7)];  // 128-query block
@@ -273,7 +313,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     // tile kt landed (only tile kt+1's direct loads may still be in flight)
     if (kt + 1 < n_kt) pf_wait_vm<NPEND>();
     else pf_wait_vm<0>();
-    __syncthreads();
+    pf_barrier();
     // the stage of tile kt+2 was last read in tile kt-1: every wave is past it
     if constexpr (V_F8) {
       if (kt + 1 < n_kt) vload(kt + 1);
@@ -451,9 +491,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 }
 
 template <int D, bool I8, bool F8>
-static bool launch_t(const PrefillArgs& a, bool o_bf16, int max_seqlen_q, hipStream_t s) {
+static bool launch_t(const PrefillArgs& args, bool o_bf16, int max_seqlen_q, hipStream_t s) {
   const int tiles = (max_seqlen_q + PfShape<D>::BM - 1) / PfShape<D>::BM;
-  dim3 grid((unsigned)(a.batch * a.hq), (unsigned)tiles);
+  if ((long)args.batch * args.hq * tiles > 0x7FFFFFFFL) return false;
+  PrefillArgs a = args;
+  // blocks of PF_TBLK_WGS / group tiles: about that many workgroups of one
+  // (sequence, kv head) stream run side by side on an XCD
+  a.tblk = max(1, PF_TBLK_WGS / (a.hq / a.hkv));
+  dim3 grid((unsigned)(a.batch * a.hq * tiles));
   if (o_bf16)
     hipLaunchKernelGGL((k_prefill<D, I8, F8, true>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   else

@@ -65,6 +65,10 @@ def test_v_permute_validation():
     assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_INT8_PER_BLOCK, None, FAKE, FAKE, None) == -1
     assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_FP8_PER_HEAD, None, FAKE, None, None) == -1
     assert "v_scales" in _err()
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_FP8_PER_HEAD_WIDE, None, FAKE, None,
+                                  None) == -1
+    assert "v_scales" in _err()
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, 7, None, FAKE, FAKE, None) != 0
 
 
 def test_append_validation():
