@@ -19,19 +19,6 @@ def _round_up(x: int, m: int) -> int:
     return (x + m - 1) // m * m
 
 
-def _fork(side, cur):
-    """Start a second stream after the work queued so far on cur."""
-    if side is not None:
-        side.wait_stream(cur)
-    return side if side is not None else cur
-
-
-def _join(side, cur):
-    """Make cur wait for everything queued on side."""
-    if side is not None:
-        cur.wait_stream(side)
-
-
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return A.BF16
@@ -47,7 +34,7 @@ class Fp8Prefill:
     which the prefill stages without a widening step."""
 
     def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True,
-                 out_dtype=torch.bfloat16, want_lse=False, amax=None, wide_v=True, overlap=True):
+                 out_dtype=torch.bfloat16, want_lse=False, amax=None, wide_v=True):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
@@ -66,23 +53,17 @@ class Fp8Prefill:
         self.vs = torch.empty(self.hkv, dtype=torch.float32, device=dev)
         self.o = torch.empty((self.t, self.hq, self.d), dtype=out_dtype, device=dev)
         self.lse = torch.empty((self.hq, self.t), dtype=torch.float32, device=dev) if want_lse else None
-        # K and V are quantized on a second stream, beside Q: the three
-        # launches are independent and each alone leaves the GPU partly idle
-        self.side = torch.cuda.Stream(device=dev) if overlap else None
 
     def quantize(self):
         dt = _dtype_code(self.q)
         aq, ak, av = self.amax if self.amax is not None else (None, None, None)
-        cur = torch.cuda.current_stream(self.q.device)
-        side = _fork(self.side, cur)
         A.attn_quant_qk(self.q, dt, self.cu, self.b, self.max_seqlen, self.t, self.hq, self.d,
-                        A.Q_FP8_PER_HEAD, 128, aq, self.qc, self.qs, stream=cur)
+                        A.Q_FP8_PER_HEAD, 128, aq, self.qc, self.qs)
         A.attn_quant_qk(self.k, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d,
-                        A.Q_FP8_PER_HEAD, 128, ak, self.kc, self.ks, stream=side)
+                        A.Q_FP8_PER_HEAD, 128, ak, self.kc, self.ks)
         A.attn_quant_v_permute(self.v, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
                                self.d, A.Q_FP8_PER_HEAD_WIDE if self.wide_v else A.Q_FP8_PER_HEAD,
-                               av, self.vp, self.vs, stream=side)
-        _join(self.side, cur)
+                               av, self.vp, self.vs)
 
     def attend(self):
         A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3,
@@ -101,8 +82,7 @@ class SagePrefill:
     """SageAttention-style flow: per-128-token-block int8 Q/K, fp16 V in the
     permuted transposed layout, int8 QK / fp16 PV prefill, fp16 output."""
 
-    def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False,
-                 overlap=True):
+    def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
@@ -119,20 +99,15 @@ class SagePrefill:
                               dtype=torch.float16, device=dev)
         self.o = torch.empty((self.t, self.hq, self.d), dtype=torch.float16, device=dev)
         self.lse = torch.empty((self.hq, self.t), dtype=torch.float32, device=dev) if want_lse else None
-        # K and V are quantized on a second stream, beside Q
-        self.side = torch.cuda.Stream(device=dev) if overlap else None
 
     def quantize(self):
         dt = _dtype_code(self.q)
-        cur = torch.cuda.current_stream(self.q.device)
-        side = _fork(self.side, cur)
         A.attn_quant_qk(self.q, dt, self.cu, self.b, self.max_seqlen, self.t, self.hq, self.d,
-                        A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs, stream=cur)
+                        A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs)
         A.attn_quant_qk(self.k, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d,
-                        A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks, stream=side)
+                        A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
         A.attn_quant_v_permute(self.v, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
-                               self.d, A.Q_NONE, None, self.vp, None, stream=side)
-        _join(self.side, cur)
+                               self.d, A.Q_NONE, None, self.vp, None)
 
     def attend(self):
         A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.INT8, A.FP16, self.qs, self.ks, None,
