@@ -54,7 +54,9 @@ typedef enum {
   ATTNQ_Q_FP8_PER_HEAD = 0,   /* fp8 e4m3fn codes, one fp32 descale per head */
   ATTNQ_Q_INT8_PER_BLOCK = 1, /* int8 codes, one fp32 scale per (seq, head, 128-token block) */
   ATTNQ_Q_NONE = 2,           /* unquantized 16-bit data */
-  ATTNQ_Q_FP8_PER_HEAD_WIDE = 3 /* fp8 e4m3fn codes as above, each stored as its exact fp16 value */
+  ATTNQ_Q_FP8_PER_HEAD_WIDE = 3, /* fp8 e4m3fn codes as above, each stored as its exact fp16 value */
+  ATTNQ_Q_INT8_PER_BLOCK_RAW_Q = 4 /* attn_prefill_varlen only: 16-bit Q quantized inside the call as
+                                      INT8_PER_BLOCK, int8 per-block K */
 } attnq_qmode;
 
 int attnq_abi_version(void);
@@ -142,7 +144,14 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  *   q [total_q, num_q_heads, head_dim] and k [total_k, num_kv_heads, head_dim]:
  *     qk_dtype FP8E4M3 with scale_mode FP8_PER_HEAD (q_scale [Hq], k_scale [Hkv]), or
  *     qk_dtype INT8 with scale_mode INT8_PER_BLOCK (q_scale [B, Hq, ceil(max_seqlen_q/128)],
- *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk).
+ *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk), or
+ *     qk_dtype BF16 / FP16 with scale_mode INT8_PER_BLOCK_RAW_Q: q is the unquantized
+ *     16-bit tensor of that type and k the int8 codes with k_scale as above.  Each
+ *     128-query block (counted from its sequence's start) is quantized inside the
+ *     call to exactly the codes and scale attn_quant_qk INT8_PER_BLOCK produces, so
+ *     the result equals quantize-then-attend; q_scale is then an optional OUTPUT
+ *     [B, Hq, ceil(max_seqlen_q/128)] receiving the scale of every block that holds
+ *     a query (other entries are left as they are).  The codes never reach memory.
  *   v_perm: attn_quant_v_permute's output for the keys, [B, Hkv, D, round_up(max_seqlen_k,128)];
  *     v_dtype FP8E4M3 (v_scale [Hkv] required) or FP16 (v_scale optional: when
  *     given, V = value * v_scale[kv head], as for FP8_PER_HEAD_WIDE).  The padding

@@ -14,6 +14,7 @@ import os
 
 __all__ = [
     "BF16", "FP16", "FP8E4M3", "INT8", "Q_FP8_PER_HEAD", "Q_INT8_PER_BLOCK", "Q_NONE", "Q_FP8_PER_HEAD_WIDE",
+    "Q_INT8_PER_BLOCK_RAW_Q",
     "library_path", "lib", "abi_version",
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
     "attn_decode_paged_workspace_size", "attn_decode_paged",
@@ -22,7 +23,7 @@ __all__ = [
 ]
 
 BF16, FP16, FP8E4M3, INT8 = 0, 1, 2, 3
-Q_FP8_PER_HEAD, Q_INT8_PER_BLOCK, Q_NONE, Q_FP8_PER_HEAD_WIDE = 0, 1, 2, 3
+Q_FP8_PER_HEAD, Q_INT8_PER_BLOCK, Q_NONE, Q_FP8_PER_HEAD_WIDE, Q_INT8_PER_BLOCK_RAW_Q = 0, 1, 2, 3, 4
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

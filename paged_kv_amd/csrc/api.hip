@@ -190,8 +190,12 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
           "num_q_heads must be a positive multiple of num_kv_heads");
   const bool fp8qk = qk_dtype == ATTNQ_FP8E4M3 && scale_mode == ATTNQ_Q_FP8_PER_HEAD;
   const bool i8qk = qk_dtype == ATTNQ_INT8 && scale_mode == ATTNQ_Q_INT8_PER_BLOCK;
-  REQUIRE(fp8qk || i8qk, ATTNQ_EUNSUPPORTED,
-          "supported Q/K: FP8E4M3 with FP8_PER_HEAD scales or INT8 with INT8_PER_BLOCK scales");
+  const bool rawq = is16(qk_dtype) && scale_mode == ATTNQ_Q_INT8_PER_BLOCK_RAW_Q;
+  REQUIRE(fp8qk || i8qk || rawq, ATTNQ_EUNSUPPORTED,
+          "supported Q/K: FP8E4M3 with FP8_PER_HEAD scales, INT8 with INT8_PER_BLOCK scales, "
+          "or BF16/FP16 Q with INT8_PER_BLOCK_RAW_Q");
+  REQUIRE(!rawq || (long)num_q_heads * head_dim < (1L << 22), ATTNQ_EUNSUPPORTED,
+          "INT8_PER_BLOCK_RAW_Q: num_q_heads * head_dim must stay below 2^22");
   REQUIRE(v_dtype == ATTNQ_FP8E4M3 || v_dtype == ATTNQ_FP16, ATTNQ_EUNSUPPORTED, "v_dtype must be FP8E4M3 or FP16");
   REQUIRE(is16(o_dtype), ATTNQ_EUNSUPPORTED, "o_dtype must be BF16 or FP16");
   REQUIRE(batch >= 0 && max_seqlen_q >= 0 && max_seqlen_k >= 0 && total_q >= 0 && total_k >= 0,
@@ -205,7 +209,8 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
   REQUIRE_PTR(cu_seqlens_q, 4);
   REQUIRE_PTR(cu_seqlens_k, 4);
-  REQUIRE_PTR(q_scale, 4);
+  if (rawq) REQUIRE_OPT_PTR(q_scale, 4);  // an output in this mode
+  else REQUIRE_PTR(q_scale, 4);
   REQUIRE_PTR(k_scale, 4);
   if (v_dtype == ATTNQ_FP8E4M3) REQUIRE_PTR(v_scale, 4);
   else REQUIRE_OPT_PTR(v_scale, 4);
@@ -223,6 +228,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
   a.o = o; a.lse = lse;
+  a.q_scale_out = rawq ? const_cast<float*>(q_scale) : nullptr;
   a.batch = batch; a.hq = num_q_heads; a.hkv = num_kv_heads;
   a.s_pad = round_up(max_seqlen_k, 128);
   a.nblk_q = (max_seqlen_q + 127) / 128;
@@ -233,7 +239,10 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   a.max_k = max_seqlen_k;
   a.sm_scale_log2 = sm_scale * LOG2E;
   if (total_q == 0) return ok();
-  LAUNCHED(attnq::launch_prefill(a, head_dim, i8qk, v_dtype == ATTNQ_FP8E4M3, o_dtype == ATTNQ_BF16,
+  const int q_mode = fp8qk ? attnq::PF_Q_FP8
+                   : i8qk  ? attnq::PF_Q_I8
+                   : qk_dtype == ATTNQ_BF16 ? attnq::PF_Q_RAW_BF16 : attnq::PF_Q_RAW_F16;
+  LAUNCHED(attnq::launch_prefill(a, head_dim, q_mode, v_dtype == ATTNQ_FP8E4M3, o_dtype == ATTNQ_BF16,
                                  max_seqlen_q, stream));
   return ok();
 }

@@ -39,12 +39,17 @@ struct PrefillArgs {
   const int32_t* cu_k;
   void* o;
   float* lse;
+  float* q_scale_out;     // 16-bit Q quantized in the kernel: block scales written here (nullable)
   int batch, hq, hkv, s_pad, nblk_q, nblk_k, total_q, total_k, causal, max_q, max_k;
   int tblk;               // query tiles per block of the workgroup order (set by launch_prefill)
   float sm_scale_log2;    // sm_scale * log2(e)
 };
-// qk_int8: int8 per-block Q/K (else fp8 per-head); v_fp8: fp8 V (else fp16 V)
-bool launch_prefill(const PrefillArgs& a, int head_dim, bool qk_int8, bool v_fp8, bool o_bf16,
+// Q/K forms of the prefill: fp8 codes with per-head descales; int8 codes with
+// per-block scales; or 16-bit Q (fp16 / bf16) that the kernel quantizes to
+// int8 per 128-query block itself, with int8 per-block K
+enum { PF_Q_FP8 = 0, PF_Q_I8 = 1, PF_Q_RAW_F16 = 2, PF_Q_RAW_BF16 = 3 };
+// q_mode: one of PF_Q_*; v_fp8: fp8 V (else fp16 V)
+bool launch_prefill(const PrefillArgs& a, int head_dim, int q_mode, bool v_fp8, bool o_bf16,
                     int max_seqlen_q, hipStream_t s);
 
 struct DecodeArgs {

@@ -168,10 +168,13 @@ ATTNQ_DEV void pf_work_item(const PrefillArgs& a, int ntiles, int lin, int& b, i
   }
 }
 
-template <int D, bool QK_I8, bool V_F8, bool O_BF16>
+template <int D, int QM, bool V_F8, bool O_BF16>
 __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const PrefillArgs a) {
   using G = PfGeo<D, V_F8>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
+  constexpr bool QK_I8 = QM != PF_Q_FP8;                     // int8 QK MFMA
+  constexpr bool Q_RAW = QM == PF_Q_RAW_F16 || QM == PF_Q_RAW_BF16;  // Q quantized here
+  // the DMA ring, then 4 floats for the block-amax exchange of a raw Q
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS + 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -198,14 +201,28 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   const int wave_kend = a.causal ? min(Lk, wq0 + 32 + off) : Lk;
 
   // ---- Q operand (B of S^T = K Q^T): lane (n, g) holds d in [g*D/4, (g+1)*D/4)
-  constexpr int QB = D / 4;  // bytes per lane
+  constexpr int QB = D / 4;  // codes (bytes) per lane and row
   v4i qop[2][2];             // [query block][16-byte half]
   int lim[2];                // per-lane key limit (exclusive) of query row qb
+  u32x4 qx[2][Q_RAW ? QB / 8 : 1];  // raw 16-bit Q: QB values per row, 8 per chunk
+  // raw Q rows of this workgroup's 128 queries (this head): the range ends
+  // at the sequence's last query
+  const int qstride = a.hq * D * 2;  // bytes per token
+  const __amdgpu_buffer_rsrc_t qrs =
+      pf_rsrc(static_cast<const uint8_t*>(a.q) + ((long)(q0 + qs) * a.hq + h) * D * (Q_RAW ? 2 : 1),
+              Q_RAW ? (uint32_t)((min(Lq - qs, BM) - 1) * qstride + D * 2) : 0u);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = wq0 + qb * 16 + n;
     qop[qb][0] = qop[qb][1] = v4i{0, 0, 0, 0};
-    if (row < Lq) {
+    if constexpr (Q_RAW) {
+      // unconditional buffer loads; rows past the sequence end read as zeros
+      // (they stay out of the block amax and encode to 0)
+#pragma unroll
+      for (int c = 0; c < QB / 8; ++c)
+        qx[qb][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  qrs, (uint32_t)((row - qs) * qstride + (g * QB + c * 8) * 2), 0u, 0));
+    } else if (row < Lq) {
       const uint8_t* src = static_cast<const uint8_t*>(a.q) + ((long)(q0 + row) * a.hq + h) * D + g * QB;
       qop[qb][0] = *reinterpret_cast<const v4i*>(src);
       if constexpr (QB == 32) qop[qb][1] = *reinterpret_cast<const v4i*>(src + 16);
@@ -214,18 +231,23 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   }
   // Q has landed before the first tile load is issued.  Otherwise the
   // compiler, unable to tell the Q loads from the tile loads in flight in the
-  // loop, drains the next tile's loads before every tile's first MFMA.
-  pf_wait_vm<0>();
+  // loop, drains the next tile's loads before every tile's first MFMA.  (A raw
+  // Q is waited for after the first tiles' loads are issued, below.)
+  if constexpr (!Q_RAW) pf_wait_vm<0>();
 
-  float q_sc;
-  if constexpr (QK_I8) q_sc = a.q_scale[((long)b * a.hq + h) * a.nblk_q + (wq0 >> 7)];  // 128-query block
-  else q_sc = a.q_scale[h];
+  float q_sc = 1.0f;
+  if constexpr (Q_RAW) {
+  } else if constexpr (QK_I8) {
+    q_sc = a.q_scale[((long)b * a.hq + h) * a.nblk_q + (wq0 >> 7)];  // 128-query block
+  } else {
+    q_sc = a.q_scale[h];
+  }
   const float k_sc_head = QK_I8 ? 0.0f : a.k_scale[hk];
   // int8: one scale per 128-key block, read through the scalar cache (the
   // constant address space) so no vector-memory wait joins the tile loads
   const __attribute__((address_space(4))) float* k_sc_blk =
       (const __attribute__((address_space(4))) float*)(uintptr_t)(a.k_scale + ((long)b * a.hkv + hk) * a.nblk_k);
-  const float base_fold = a.sm_scale_log2 * q_sc;
+  float base_fold = a.sm_scale_log2 * q_sc;
 
   // ---- tile sources as buffer descriptors: K rows of this (sequence, kv head)
   // with the range ending at the last key (rows past it arrive as zeros), and
@@ -302,11 +324,69 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 
   // ---- prologue: tiles 0 and 1 in flight
   constexpr int NPEND = G::NKD + G::NVD;  // direct loads per wave per tile
-  if (n_kt > 0) {
+  if constexpr (Q_RAW && !V_F8) {
+    // unconditional, so that one wait below counts them: loads past the last
+    // key read zeros (range-checked descriptors) into stages no tile uses
+    pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
+    pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
+  } else if (n_kt > 0) {
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
     if constexpr (V_F8) vload(0);
     if (n_kt > 1) pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
   }
+  if constexpr (Q_RAW) {
+    // This workgroup's 128 queries are one quantization block (128 tokens
+    // from the sequence start): scale = amax/127 over the block, codes =
+    // clamp(rint(x / scale), -127, 127), the codes and scale attn_quant_qk
+    // writes in INT8_PER_BLOCK mode (same arithmetic, same helpers).  The Q
+    // loads went out before the first tiles' loads: wait for them only.
+    if constexpr (V_F8) pf_wait_vm<0>();
+    else pf_wait_vm<2 * NPEND>();
+    constexpr bool BF = QM == PF_Q_RAW_BF16;
+    float m = 0.0f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int c = 0; c < QB / 8; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m = fmaxf(m, fabsf(h16_to_f32(qx[qb][c][e] & 0xffffu, BF)));
+          m = fmaxf(m, fabsf(h16_to_f32(qx[qb][c][e] >> 16, BF)));
+        }
+    m = wave_max(m);
+    float* s_amax = reinterpret_cast<float*>(smem + G::LDS);
+    if (lane == 0) s_amax[wave] = m;
+    pf_barrier();
+    const float amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+    const float scale = amax == 0.0f ? 1.0f : amax / 127.0f;
+    if (a.q_scale_out != nullptr && threadIdx.x == 0)
+      a.q_scale_out[((long)b * a.hq + h) * a.nblk_q + tile] = scale;
+    const float rs = 1.0f / scale;
+    auto encode = [&](auto fast_c) {
+      constexpr bool FAST = decltype(fast_c)::value;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int c = 0; c < QB / 8; ++c)
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t bits = (qx[qb][c][2 * w + j / 2] >> (16 * (j & 1))) & 0xffffu;
+              const float xv = h16_to_f32(bits, BF);
+              const uint32_t code = (uint32_t)int8_encode(FAST ? quot_by_recip(xv, scale, rs) : xv / scale) & 0xffu;
+              word |= code << (8 * j);
+            }
+            qop[qb][c >> 1][(c & 1) * 2 + w] = (int)word;
+          }
+    };
+    if (scale >= QUOT_MIN_SCALE) encode(std::true_type{});  // uniform
+    else encode(std::false_type{});
+    q_sc = scale;
+    base_fold = a.sm_scale_log2 * q_sc;
+  }
+
   int kst = 0;  // K (and DMA'd V^T) stage of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
     if constexpr (V_F8) vstore(kt & 1);
@@ -490,7 +570,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   }
 }
 
-template <int D, bool I8, bool F8>
+template <int D, int QM, bool F8>
 static bool launch_t(const PrefillArgs& args, bool o_bf16, int max_seqlen_q, hipStream_t s) {
   const int tiles = (max_seqlen_q + PfShape<D>::BM - 1) / PfShape<D>::BM;
   if ((long)args.batch * args.hq * tiles > 0x7FFFFFFFL) return false;
@@ -500,21 +580,33 @@ static bool launch_t(const PrefillArgs& args, bool o_bf16, int max_seqlen_q, hip
   a.tblk = max(1, PF_TBLK_WGS / (a.hq / a.hkv));
   dim3 grid((unsigned)(a.batch * a.hq * tiles));
   if (o_bf16)
-    hipLaunchKernelGGL((k_prefill<D, I8, F8, true>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<D, QM, F8, true>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_prefill<D, I8, F8, false>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<D, QM, F8, false>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
 
-bool launch_prefill(const PrefillArgs& a, int head_dim, bool qk_int8, bool v_fp8, bool o_bf16,
+template <int D, int QM>
+static bool launch_v(const PrefillArgs& a, bool v_fp8, bool o_bf16, int max_seqlen_q, hipStream_t s) {
+  return v_fp8 ? launch_t<D, QM, true>(a, o_bf16, max_seqlen_q, s) : launch_t<D, QM, false>(a, o_bf16, max_seqlen_q, s);
+}
+
+template <int D>
+static bool launch_q(const PrefillArgs& a, int q_mode, bool v_fp8, bool o_bf16, int max_seqlen_q, hipStream_t s) {
+  switch (q_mode) {
+    case PF_Q_FP8: return launch_v<D, PF_Q_FP8>(a, v_fp8, o_bf16, max_seqlen_q, s);
+    case PF_Q_I8: return launch_v<D, PF_Q_I8>(a, v_fp8, o_bf16, max_seqlen_q, s);
+    case PF_Q_RAW_F16: return launch_v<D, PF_Q_RAW_F16>(a, v_fp8, o_bf16, max_seqlen_q, s);
+    case PF_Q_RAW_BF16: return launch_v<D, PF_Q_RAW_BF16>(a, v_fp8, o_bf16, max_seqlen_q, s);
+    default: return false;
+  }
+}
+
+bool launch_prefill(const PrefillArgs& a, int head_dim, int q_mode, bool v_fp8, bool o_bf16,
                     int max_seqlen_q, hipStream_t s) {
   if (max_seqlen_q <= 0 || a.batch <= 0) return true;
-  if (head_dim == 128) {
-    if (qk_int8) return v_fp8 ? launch_t<128, true, true>(a, o_bf16, max_seqlen_q, s) : launch_t<128, true, false>(a, o_bf16, max_seqlen_q, s);
-    return v_fp8 ? launch_t<128, false, true>(a, o_bf16, max_seqlen_q, s) : launch_t<128, false, false>(a, o_bf16, max_seqlen_q, s);
-  }
-  if (qk_int8) return v_fp8 ? launch_t<64, true, true>(a, o_bf16, max_seqlen_q, s) : launch_t<64, true, false>(a, o_bf16, max_seqlen_q, s);
-  return v_fp8 ? launch_t<64, false, true>(a, o_bf16, max_seqlen_q, s) : launch_t<64, false, false>(a, o_bf16, max_seqlen_q, s);
+  return head_dim == 128 ? launch_q<128>(a, q_mode, v_fp8, o_bf16, max_seqlen_q, s)
+                         : launch_q<64>(a, q_mode, v_fp8, o_bf16, max_seqlen_q, s);
 }
 
 }  // namespace attnq

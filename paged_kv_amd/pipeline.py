@@ -80,9 +80,13 @@ class Fp8Prefill:
 
 class SagePrefill:
     """SageAttention-style flow: per-128-token-block int8 Q/K, fp16 V in the
-    permuted transposed layout, int8 QK / fp16 PV prefill, fp16 output."""
+    permuted transposed layout, int8 QK / fp16 PV prefill, fp16 output.
+    With fuse_q (default) the prefill quantizes each 128-query block of the
+    16-bit Q itself (same codes and scales as attn_quant_qk; the scales land
+    in qs) instead of reading int8 codes written by a separate pass."""
 
-    def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False):
+    def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False,
+                 fuse_q=True):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
@@ -90,8 +94,11 @@ class SagePrefill:
         self.b = cu_seqlens.numel() - 1
         self.max_seqlen = int(max_seqlen)
         self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        self.fuse_q = bool(fuse_q)
+        if v.dtype != torch.float16:
+            raise TypeError("SagePrefill takes fp16 V (the PV product runs on fp16 V^T)")
         nblk = (self.max_seqlen + 127) // 128
-        self.qc = torch.empty(q.shape, dtype=torch.int8, device=dev)
+        self.qc = None if self.fuse_q else torch.empty(q.shape, dtype=torch.int8, device=dev)
         self.kc = torch.empty(k.shape, dtype=torch.int8, device=dev)
         self.qs = torch.empty((self.b, self.hq, nblk), dtype=torch.float32, device=dev)
         self.ks = torch.empty((self.b, self.hkv, nblk), dtype=torch.float32, device=dev)
@@ -101,17 +108,21 @@ class SagePrefill:
         self.lse = torch.empty((self.hq, self.t), dtype=torch.float32, device=dev) if want_lse else None
 
     def quantize(self):
-        dt = _dtype_code(self.q)
-        A.attn_quant_qk(self.q, dt, self.cu, self.b, self.max_seqlen, self.t, self.hq, self.d,
-                        A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs)
-        A.attn_quant_qk(self.k, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d,
-                        A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
-        A.attn_quant_v_permute(self.v, dt, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
+        if not self.fuse_q:
+            A.attn_quant_qk(self.q, _dtype_code(self.q), self.cu, self.b, self.max_seqlen, self.t,
+                            self.hq, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs)
+        A.attn_quant_qk(self.k, _dtype_code(self.k), self.cu, self.b, self.max_seqlen, self.t,
+                        self.hkv, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
+        A.attn_quant_v_permute(self.v, A.FP16, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
                                self.d, A.Q_NONE, None, self.vp, None)
 
     def attend(self):
-        A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.INT8, A.FP16, self.qs, self.ks, None,
-                              A.Q_INT8_PER_BLOCK, self.cu, self.cu, self.b, self.max_seqlen,
+        if self.fuse_q:
+            q, qk_dtype, mode = self.q, _dtype_code(self.q), A.Q_INT8_PER_BLOCK_RAW_Q
+        else:
+            q, qk_dtype, mode = self.qc, A.INT8, A.Q_INT8_PER_BLOCK
+        A.attn_prefill_varlen(q, self.kc, self.vp, qk_dtype, A.FP16, self.qs, self.ks, None,
+                              mode, self.cu, self.cu, self.b, self.max_seqlen,
                               self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
                               self.sm_scale, self.causal, self.o, A.FP16, self.lse)
 

@@ -104,6 +104,14 @@ def test_prefill_validation():
     assert _prefill(cq=None) == -1
     assert _prefill(vs=None) == -1 and "v_scale" in _err()
     assert _prefill(mk=1 << 21, hkv=8, hq=8) == -2 and "2 GiB" in _err()   # 32-bit tile offsets
+    # 16-bit Q quantized inside the call: only with INT8_PER_BLOCK_RAW_Q, which takes no codes
+    raw = dict(vd=pk.FP16, mode=pk.Q_INT8_PER_BLOCK_RAW_Q)
+    assert _prefill(qk=pk.FP16, mode=pk.Q_INT8_PER_BLOCK) == -2
+    assert _prefill(qk=pk.INT8, **raw) == -2
+    assert _prefill(qk=pk.FP8E4M3, **raw) == -2
+    # q_scale is an optional output there; k_scale stays required
+    assert _prefill(qk=pk.BF16, qs=None, ks=None, **raw) == -1 and "k_scale" in _err()
+    assert _prefill(qk=pk.FP16, qs=FAKE + 2, **raw) == -1 and "q_scale" in _err()
 
 
 def _decode(**kw):

@@ -81,12 +81,12 @@ def test_fp8_deterministic():
     assert np.array_equal(from_dev_bits(p.o), a)
 
 
-def _sage_flow(x, sm_scale, causal=True):
+def _sage_flow(x, sm_scale, causal=True, fuse_q=True):
     from paged_kv_amd.pipeline import SagePrefill
     cu = x["cu_seqlens"]
     mx = int(np.diff(cu).max())
     p = SagePrefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(cu), mx, sm_scale,
-                    causal=causal, want_lse=True)
+                    causal=causal, want_lse=True, fuse_q=fuse_q)
     p.run()
     torch.cuda.synchronize()
     return p, mx
@@ -99,15 +99,30 @@ def _sage_ref(x, mx, sm_scale, causal, rows=None, seqs=None):
     return qc, qs, kc, ks
 
 
+def _qs_written(qs, cu):
+    """Mask of the per-block scale entries that hold a query (the fused flow
+    writes only those)."""
+    m = np.zeros(qs.shape, bool)
+    for b, L in enumerate(np.diff(cu)):
+        m[b, :, :(int(L) + 127) // 128] = True
+    return m
+
+
+@pytest.mark.parametrize("fuse_q", [True, False])
 @pytest.mark.parametrize("lens", [[130, 257, 1, 511], [64, 0, 700]])
-def test_sage_int8_small(lens):
+def test_sage_int8_small(lens, fuse_q):
     x = gen.sage_inputs(41, lens, 8, 2, 128)
     sm = 1 / math.sqrt(128)
-    p, mx = _sage_flow(x, sm)
+    p, mx = _sage_flow(x, sm, fuse_q=fuse_q)
     cu = x["cu_seqlens"]
     qc, qs, kc, ks = _sage_ref(x, mx, sm, True)
-    assert np.array_equal(p.qc.cpu().numpy(), qc) and np.array_equal(p.kc.cpu().numpy(), kc)
-    assert np.array_equal(p.qs.cpu().numpy().view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(p.kc.cpu().numpy(), kc)
+    if fuse_q:  # Q codes stay inside the prefill; its block scales are output
+        w = _qs_written(qs, cu)
+        assert np.array_equal(p.qs.cpu().numpy().view(np.uint32)[w], qs.view(np.uint32)[w])
+    else:
+        assert np.array_equal(p.qc.cpu().numpy(), qc)
+        assert np.array_equal(p.qs.cpu().numpy().view(np.uint32), qs.view(np.uint32))
     vperm, _ = v_permute(x["v"], "fp16", cu, mx, fp8=False)
     assert np.array_equal(p.vp.cpu().numpy().view(np.uint16), vperm.view(np.uint16))
     ref = prefill_varlen(dequant_int8_per_block(qc, qs, cu), dequant_int8_per_block(kc, ks, cu),
@@ -115,6 +130,38 @@ def test_sage_int8_small(lens):
     got = decode_out(from_dev_bits(p.o), "fp16")
     compare_outputs(got, ref["o"], ref["o_exact"], "fp16", f"sage {lens}")
     compare_lse(p.lse.cpu().numpy(), ref["lse"], "sage")
+
+
+@pytest.mark.parametrize("case", ["config2", "d64_bf16", "ragged_gqa"])
+def test_sage_fused_q_equals_separate_quant(case):
+    """Quantizing Q inside the prefill gives bit-identical outputs, lse and
+    block scales to attn_quant_qk followed by the prefill (same codes)."""
+    from paged_kv_amd.pipeline import SagePrefill
+    if case == "config2":
+        x, sm = gen.config2(), 1 / math.sqrt(128)
+    elif case == "d64_bf16":  # bf16 Q (and K), fp16 V
+        x, sm = gen.sage_inputs(44, [300, 129, 1000], 4, 4, 64), 0.125
+        for t in ("q", "k"):  # truncated to bf16 bit patterns
+            x[t] = (as_f32(x[t], "fp16").view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        x, sm = gen.sage_inputs(45, [1, 127, 128, 129, 383, 0, 2049], 12, 4, 128), 0.07
+    cu = x["cu_seqlens"]
+    mx = int(np.diff(cu).max())
+    q, k, v = (to_dev(x[t]) for t in ("q", "k", "v"))
+    outs = []
+    for fuse in (True, False):
+        p = SagePrefill(q, k, v, to_dev(cu), mx, sm, causal=True, want_lse=True, fuse_q=fuse)
+        if fuse:
+            p.qs.fill_(-1.0)
+        p.run()
+        torch.cuda.synchronize()
+        outs.append((from_dev_bits(p.o).copy(), p.lse.cpu().numpy().copy(), p.qs.cpu().numpy().copy()))
+    (o1, l1, s1), (o2, l2, s2) = outs
+    w = _qs_written(s2, cu)
+    assert np.array_equal(s1.view(np.uint32)[w], s2.view(np.uint32)[w])
+    assert np.all(s1[~w] == -1.0)  # entries without a query are left alone
+    assert np.array_equal(o1, o2)
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
 def _sampled_rows(rng, L, n=12):
@@ -132,8 +179,9 @@ def test_config2_full_size_sampled():
     p, mx = _sage_flow(x, sm)
     cu = x["cu_seqlens"]
     qc, qs, kc, ks = _sage_ref(x, mx, sm, True)
-    assert np.array_equal(p.qc.cpu().numpy(), qc) and np.array_equal(p.kc.cpu().numpy(), kc)
-    assert np.array_equal(p.qs.cpu().numpy().view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(p.kc.cpu().numpy(), kc)
+    w = _qs_written(qs, cu)
+    assert np.array_equal(p.qs.cpu().numpy().view(np.uint32)[w], qs.view(np.uint32)[w])
     assert np.array_equal(p.ks.cpu().numpy().view(np.uint32), ks.view(np.uint32))
     got_all = decode_out(from_dev_bits(p.o), "fp16")
     lse_all = p.lse.cpu().numpy()
