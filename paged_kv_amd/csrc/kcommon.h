@@ -93,10 +93,22 @@ ATTNQ_DEV float quot_by_recip(float x, float s, float r) {
 }
 constexpr float QUOT_MIN_SCALE = 1e-30f;
 
+// The same quotient without the sign fix-up of a zero result, for int8 codes:
+// rint(+0) and rint(-0) give the same code.
+ATTNQ_DEV float quot_by_recip_i8(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_fmaf(e, r, q0);
+}
+
+// rint(v) (ties to even) clamped to [-127, 127]; NaN -> 0.  v_cvt_i32_f32
+// saturates out-of-range values and maps NaN to 0, so one integer clamp
+// after it finishes the job (a C cast of NaN or of an out-of-range float
+// would be undefined).
 ATTNQ_DEV int32_t int8_encode(float v) {
-  float r = __builtin_rintf(v);
-  r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
-  return (int32_t)r;
+  int32_t i;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(__builtin_rintf(v)));
+  return i > 127 ? 127 : (i < -127 ? -127 : i);
 }
 
 // ---------------------------------------------------------------- reductions

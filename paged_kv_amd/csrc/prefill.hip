@@ -375,7 +375,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
             for (int j = 0; j < 4; ++j) {
               const uint32_t bits = (qx[qb][c][2 * w + j / 2] >> (16 * (j & 1))) & 0xffffu;
               const float xv = h16_to_f32(bits, BF);
-              const uint32_t code = (uint32_t)int8_encode(FAST ? quot_by_recip(xv, scale, rs) : xv / scale) & 0xffu;
+              const uint32_t code = (uint32_t)int8_encode(FAST ? quot_by_recip_i8(xv, scale, rs) : xv / scale) & 0xffu;
               word |= code << (8 * j);
             }
             qop[qb][c >> 1][(c & 1) * 2 + w] = (int)word;

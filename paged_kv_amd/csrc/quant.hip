@@ -171,7 +171,7 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xv = h16_to_f32(e & 1 ? v[k][e >> 1] >> 16 : v[k][e >> 1] & 0xffffu, BF16);
-          q[e] = (uint32_t)int8_encode(FAST ? quot_by_recip(xv, scale, rs) : xv / scale) & 0xffu;
+          q[e] = (uint32_t)int8_encode(FAST ? quot_by_recip_i8(xv, scale, rs) : xv / scale) & 0xffu;
         }
         *reinterpret_cast<u32x2*>(codes + ((long)(r0 + row) * heads + h) * DIM + col) =
             u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24), q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
