@@ -59,9 +59,11 @@ def causal_pairs(lens) -> int:
 
 
 def time_events(fn, iters, flush=None):
-    """Per-call durations (ms) of fn() with events on the current stream."""
+    """Per-call durations (ms) of fn() with events on the current stream.  The
+    calls (and the untimed flush before each) are queued back to back and
+    synchronized once, so the GPU never idles between them."""
     import torch
-    out = []
+    ev = []
     for _ in range(iters):
         if flush is not None:
             flush()
@@ -69,9 +71,9 @@ def time_events(fn, iters, flush=None):
         s.record()
         fn()
         e.record()
-        e.synchronize()
-        out.append(s.elapsed_time(e))
-    return out
+        ev.append((s, e))
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
 
 
 def settle(fn, min_ms=250.0):
@@ -262,12 +264,22 @@ def summarize_traffic(fetch_dir, write_dir, fetch_cmd, write_cmd):
         factor = (CALIB_BYTES / 1024.0) / calib
         out[name] = {"kernel_kib": pf[0], "copy_kib": calib, "factor": factor, "bytes": pf[0] * factor * 1024.0}
     traffic = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    import gen
+    lens = gen.configs.config2_lengths()
+    t, spad = int(lens.sum()), (int(lens.max()) + 127) // 128 * 128
+    unique = t * 32 * 128 * 2 + t * 8 * 128 + len(lens) * 8 * 128 * spad * 2 + t * 32 * 128 * 2 \
+        + len(lens) * 8 * (spad // 128) * 4
     h = kernel_source_hash()
     lines = [
-        "# HBM-side traffic of one k_prefill launch (int8 QK / fp16 PV, sage varlen workload)",
+        "# HBM-side traffic of one k_prefill launch (sage varlen workload: fp16 Q quantized to int8 in",
+        "# the kernel, int8 K, fp16 V^T, fp16 O)",
         "",
         "Workload: B=8, lengths U{512..4096} (seed 1002), causal, Hq=32, Hkv=8, D=128; one launch of",
-        "`attn_prefill_varlen` after `attn_quant_qk` / `attn_quant_v_permute` (bench.py --traffic-probe).",
+        "`attn_prefill_varlen` (INT8_PER_BLOCK_RAW_Q) after `attn_quant_qk` (K) and",
+        "`attn_quant_v_permute` (V) (bench.py --traffic-probe).",
+        "",
+        f"Unique bytes the launch must move: {unique:.4g} (fp16 Q + int8 K + fp16 V^T with its padding",
+        "+ fp16 O + scales), against the measured total below.",
         "",
         "Commands (from the repository root on the GPU host, `cd /tmp && export TMPDIR=/tmp` first):",
         "",
@@ -304,7 +316,8 @@ def stored_traffic():
 
 def cpu_baseline(x, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the config-2 workload: whole
-    heads of the first sequence, added until the time budget is spent."""
+    (sequence, q head) attention problems, sequence by sequence, added until
+    the time budget is spent."""
     from oracle.attention import dequant_int8_per_block, prefill_varlen
     from oracle.quant import quant_int8_per_block, as_f32
     try:
@@ -313,26 +326,32 @@ def cpu_baseline(x, budget_s=12.0):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     cu = x["cu_seqlens"]
-    L = int(cu[1])
-    one = np.array([0, L], np.int32)
-    t0 = time.perf_counter()
-    qc, qs = quant_int8_per_block(x["q"][:L], "fp16", one, L)
-    kc, ks = quant_int8_per_block(x["k"][:L], "fp16", one, L)
-    qd = dequant_int8_per_block(qc, qs, one)
-    kd = dequant_int8_per_block(kc, ks, one)
-    vd = as_f32(x["v"][:L], "fp16").astype(np.float64)
-    heads = 0
-    t_att = 0.0
-    while heads < 32 and t_att < budget_s:
-        ta = time.perf_counter()
-        prefill_varlen(qd[:, heads:heads + 1], kd[:, heads // 4:heads // 4 + 1],
-                       vd[:, heads // 4:heads // 4 + 1], one, one, x["sm_scale"], True, "fp16")
-        t_att += time.perf_counter() - ta
-        heads += 1
-    flops = 4.0 * 128 * heads * L * (L + 1) / 2
+    t_att, t_prep, flops, done = 0.0, 0.0, 0.0, []
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        L = s1 - s0
+        one = np.array([0, L], np.int32)
+        tp = time.perf_counter()
+        qc, qs = quant_int8_per_block(x["q"][s0:s1], "fp16", one, L)
+        kc, ks = quant_int8_per_block(x["k"][s0:s1], "fp16", one, L)
+        qd = dequant_int8_per_block(qc, qs, one)
+        kd = dequant_int8_per_block(kc, ks, one)
+        vd = as_f32(x["v"][s0:s1], "fp16").astype(np.float64)
+        t_prep += time.perf_counter() - tp
+        heads = 0
+        while heads < 32 and t_att < budget_s:
+            ta = time.perf_counter()
+            prefill_varlen(qd[:, heads:heads + 1], kd[:, heads // 4:heads // 4 + 1],
+                           vd[:, heads // 4:heads // 4 + 1], one, one, x["sm_scale"], True, "fp16")
+            t_att += time.perf_counter() - ta
+            heads += 1
+        flops += 4.0 * 128 * heads * L * (L + 1) / 2
+        done.append(f"{b}:L={L}x{heads}h")
+        if t_att >= budget_s:
+            break
     return {"value": flops / t_att / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"config-2 sequence 0 (L={L}), {heads} of 32 q heads, causal, fp64 numpy; "
-                      f"{t_att:.1f} s of attention (quantization {time.perf_counter() - t0 - t_att:.1f} s not counted)"}
+            "sample": f"config-2 (sequence:length x q heads) {' '.join(done)}, causal, fp64 numpy; "
+                      f"{t_att:.1f} s of attention (quantization {t_prep:.1f} s not counted)"}
 
 
 def main():
