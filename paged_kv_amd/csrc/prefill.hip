@@ -100,6 +100,8 @@ ATTNQ_DEV void pf_barrier() {
   // gfx9 s_waitcnt: lgkmcnt[11:8]=0, vmcnt[3:0]+[15:14] and expcnt[6:4] at maximum
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
+  // no LDS access of this wave moves above the barrier (no wait is needed)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // 16 fp8 codes (one u32x4) -> 16 fp16 values (exact), two u32x4.
