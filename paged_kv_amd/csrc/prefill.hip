@@ -51,6 +51,8 @@ constexpr int PF_BN = 64;   // keys per tile
 constexpr int PF_NST = 3;   // LDS stages of the DMA ring (two tiles in flight)
 constexpr int PF_TBLK_WGS = 64;  // workgroups per K/V stream in one block of the work order
 constexpr float PF_LN2 = 0.69314718055994530942f;
+constexpr float PF_I8_BIAS_F = 12582912.0f;  // 1.5 * 2^23
+constexpr int PF_I8_BIAS_BITS = 0x4B400000;  // its bits
 // buffer descriptor word 3 for untyped 32-bit accesses
 constexpr int PF_RSRC_W3 = 0x00020000;
 
@@ -424,11 +426,21 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if constexpr (QK_I8) {
-          v4i acc = v4i{0, 0, 0, 0};
+          // The accumulator starts at the bits of 1.5 * 2^23, so its integer
+          // sum s (|s| < 2^21) comes out as the bits of the float
+          // 1.5 * 2^23 + s, exactly: no int-to-float conversion per score.
+          // (Each element passes an empty asm before the bit cast: bit-casting
+          // elements of an int MFMA result straight to float makes this
+          // compiler read element 0 for all four.)
+          v4i acc = v4i{PF_I8_BIAS_BITS, PF_I8_BIAS_BITS, PF_I8_BIAS_BITS, PF_I8_BIAS_BITS};
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qop[qb][0], acc, 0, 0, 0);
           if constexpr (QB == 32) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb2, qop[qb][1], acc, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[kb][qb][r] = (float)acc[r];
+          for (int r = 0; r < 4; ++r) {
+            int bits = acc[r];
+            asm("" : "+v"(bits));
+            s[kb][qb][r] = __builtin_bit_cast(float, bits);
+          }
         } else {
           const v8i kop = v8i{ka[0], ka[1], ka[2], ka[3], kb2[0], kb2[1], kb2[2], kb2[3]};
           const v8i qo = v8i{qop[qb][0][0], qop[qb][0][1], qop[qb][0][2], qop[qb][0][3],
@@ -454,6 +466,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
       fold = base_fold * k_sc_blk[kt >> 1];
     else
       fold = base_fold * k_sc_head;
+    // the scores' bias (int8: s carries 1.5 * 2^23) in log2 units
+    const float boff = QK_I8 ? PF_I8_BIAS_F * fold : 0.0f;
 
     // ---- mask (only tiles that cross the causal diagonal or the sequence end)
     const bool need_mask = kfirst + PF_BN > min(Lk, wq0 + off + 1);
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     float lt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float neg_m = -m_ref[qb];
+      const float neg_m = -m_ref[qb] - boff;
       lt[qb] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -504,13 +518,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
           for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][qb][r]);
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if constexpr (QK_I8) m -= PF_I8_BIAS_F;           // exact (or -inf)
         const float m_new = fmaxf(m_ref[qb], m * fold);  // fold > 0
         const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) oacc[db][qb] *= alpha;
-        const float neg_m = m_new == -INFINITY ? 0.0f : -m_new;
+        const float neg_m = (m_new == -INFINITY ? 0.0f : -m_new) - boff;
         lt[qb] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
