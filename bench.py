@@ -115,25 +115,31 @@ def bench_config2(steps, warmup):
     for _ in range(warmup):
         p.run()
     torch.cuda.synchronize()
-    # timed region: every step is quantize + prefill; events on the launch
-    # stream mark each step's phases, so the prefill kernel's duration is
-    # taken in the same back-to-back run that gives the step time
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    # timed region: every step is quantize + prefill.  Events on the launch
+    # stream bracket the prefill launch of every SAMPLE-th step, so its
+    # duration is taken in the same back-to-back run that gives the step time
+    # (an event pair leaves a gap of ~6 us between kernels: sampled, not on
+    # every step)
+    SAMPLE = 4
+    picked = list(range(0, steps, SAMPLE))
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in picked}
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     s.record()
     for i in range(steps):
         p.quantize()
-        ev[i][0].record()
+        if i in ev:
+            ev[i][0].record()
         p.attend()
-        ev[i][1].record()
+        if i in ev:
+            ev[i][1].record()
     e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = s.elapsed_time(e) / steps
-    kms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
-    qms = [(s if i == 0 else ev[i - 1][1]).elapsed_time(ev[i][0]) for i in range(steps)]
+    kms = [ev[i][0].elapsed_time(ev[i][1]) for i in picked]
     kavg = float(np.mean(kms))
+    qms = time_events(p.quantize, 10)  # the quantization alone (after the timed region)
     return {
         "x": x, "lens": lens, "flops": flops, "ms_per_step": ms, "wall_s": wall,
         "kernel_ms": kavg, "kernel_ms_min": float(np.min(kms)), "quant_ms": float(np.mean(qms)),

@@ -92,23 +92,24 @@ def test_int8_per_block(lens):
         assert np.array_equal(codes.cpu().numpy(), rc), name
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("fp8,dtype", [(True, "bf16"), (False, "fp16"), (False, "bf16"), (True, "fp16")])
-def test_v_permute(fp8, dtype):
+def test_v_permute(fp8, dtype, d):
     import paged_kv_amd as pk
-    lens = [37, 64, 1, 0, 200]
+    lens = [37, 64, 1, 0, 200, 65, 131]
     if dtype == "bf16":
-        v = gen.prefill_fp8_inputs(9, lens, 2, 2, 128)["v"]
+        v = gen.prefill_fp8_inputs(9, lens, 2, 2, d)["v"]
     else:
-        v = gen.sage_inputs(9, lens, 2, 2, 128)["v"]
+        v = gen.sage_inputs(9, lens, 2, 2, d)["v"]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     mx = max(lens)
     sp = (mx + 127) // 128 * 128
     vd = to_dev(v)
-    out = torch.full((len(lens), 2, 128, sp), 0x55 if fp8 else 0, dtype=torch.uint8 if fp8 else torch.int16,
+    out = torch.full((len(lens), 2, d, sp), 0x55 if fp8 else 0, dtype=torch.uint8 if fp8 else torch.int16,
                      device="cuda")
     vs = torch.empty(2, dtype=torch.float32, device="cuda")
     pk.attn_quant_v_permute(vd, pk.BF16 if dtype == "bf16" else pk.FP16, to_dev(cu), len(lens), mx, cu[-1],
-                            2, 128, pk.Q_FP8_PER_HEAD if fp8 else pk.Q_NONE, None, out, vs if fp8 else None)
+                            2, d, pk.Q_FP8_PER_HEAD if fp8 else pk.Q_NONE, None, out, vs if fp8 else None)
     torch.cuda.synchronize()
     ref, rds = v_permute(v, dtype, cu, mx, fp8=fp8)
     got = out.cpu().numpy()
