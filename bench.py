@@ -149,7 +149,7 @@ def bench_config2(steps, warmup):
     }
 
 
-def bench_config3(iters):
+def bench_config3(iters, cpu=False):
     import torch
     import gen
     from paged_kv_amd.pipeline import PagedDecode
@@ -158,18 +158,20 @@ def bench_config3(iters):
     p = PagedDecode(to_dev(x["q"]), to_dev(x["k_cache"]), to_dev(x["v_cache"]), to_dev(x["k_scale"]),
                     to_dev(x["v_scale"]), to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]),
                     to_dev(x["kv_last_page_len"]), x["max_kv_len"], x["sm_scale"])
-    del x["k_cache"], x["v_cache"]
     kv_bytes = float(np.sum(x["kv_lens"].astype(np.int64)) * 8 * 128 * 2)
     other = 64 * 32 * 128 * 2 * 2 + x["kv_indices"].size * 4 + 65 * 4 * 2
     settle(p.run)
     ms = time_events(p.run, iters, make_flush())
     med = float(np.median(ms))
     gbs = (kv_bytes + other) / (med * 1e-3) / 1e9
-    return {"ms": med, "ms_min": float(np.min(ms)), "bytes": kv_bytes + other, "GB/s": gbs,
-            "pct_hbm": 100 * gbs / PEAK_HBM}
+    r = {"ms": med, "ms_min": float(np.min(ms)), "bytes": kv_bytes + other, "GB/s": gbs,
+         "pct_hbm": 100 * gbs / PEAK_HBM}
+    if cpu:
+        r["cpu_oracle"] = oracle_config3(x)
+    return r
 
 
-def bench_config5(iters):
+def bench_config5(iters, cpu=False):
     import torch
     import gen
     from paged_kv_amd.pipeline import AppendRopeFp8Prefill
@@ -194,13 +196,16 @@ def bench_config5(iters):
         p.k.copy_(k0)
     pipe = time_events(p.run, max(2, iters // 2), restore)
     med = float(np.median(kms))
-    return {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
-            "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
-            "pipeline_ms": float(np.median(pipe)),
-            "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12}
+    r = {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
+         "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
+         "pipeline_ms": float(np.median(pipe)),
+         "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12}
+    if cpu:
+        r["cpu_oracle"] = oracle_config5(x)
+    return r
 
 
-def bench_config4(iters):
+def bench_config4(iters, cpu=False):
     import torch
     import gen
     from paged_kv_amd.pipeline import SparseMlaDecode
@@ -216,8 +221,91 @@ def bench_config4(iters):
     ms = time_events(p.run, iters, make_flush())
     med = float(np.median(ms))
     gbs = nbytes / (med * 1e-3) / 1e9
-    return {"ms": med, "ms_min": float(np.min(ms)), "bytes": nbytes, "GB/s": gbs,
-            "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12}
+    r = {"ms": med, "ms_min": float(np.min(ms)), "bytes": nbytes, "GB/s": gbs,
+         "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12}
+    if cpu:
+        r["cpu_oracle"] = oracle_config4(x)
+    return r
+
+
+def host_cores() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def oracle_config3(x, budget_s=3.0):
+    """The fp64 oracle of the paged fp8 decode on whole sequences (all 32 q
+    heads), in batch order until the budget is spent; GB/s of fp8 K/V read."""
+    from oracle.attention import decode_paged
+    lens = x["kv_lens"].astype(np.int64)
+    t, nbytes, done = 0.0, 0.0, 0
+    while done < len(lens) and t < budget_s:
+        t0 = time.perf_counter()
+        decode_paged(x["q"], x["k_cache"], x["v_cache"], x["k_scale"], x["v_scale"], x["kv_indptr"],
+                     x["kv_indices"], x["kv_last_page_len"], x["sm_scale"], batches=[done])
+        t += time.perf_counter() - t0
+        nbytes += float(lens[done]) * 8 * 128 * 2
+        done += 1
+    return {"GB/s": nbytes / t / 1e9, "cores": host_cores(), "kind": "oracle",
+            "sample": f"sequences 0..{done - 1} of 64 ({int(lens[:done].sum())} tokens, 32 q heads), "
+                      f"fp64 numpy, {t:.1f} s"}
+
+
+def oracle_config4(x, budget_s=4.0):
+    """The fp64 oracle of the sparse MLA decode on whole (sequence, query)
+    problems (128 heads, 2048 selected rows), in batch order until the budget
+    is spent; GB/s of 656-byte cache rows read."""
+    from oracle.attention import sparse_mla_decode, MLA_ROW
+    nb = x["q"].shape[0]
+    t, rows, done = 0.0, 0, 0
+    while done < nb and t < budget_s:
+        t0 = time.perf_counter()
+        sparse_mla_decode(x["q"], x["kv_cache"], x["block_table"], x["kv_lens"], x["sparse_indices"],
+                          x["sm_scale"], batches=[done])
+        t += time.perf_counter() - t0
+        idx = np.asarray(x["sparse_indices"][done], np.int64)
+        rows += int(((idx >= 0) & (idx < int(x["kv_lens"][done]))).sum())
+        done += 1
+    return {"GB/s": rows * MLA_ROW / t / 1e9, "cores": host_cores(), "kind": "oracle",
+            "sample": f"sequences 0..{done - 1} of {nb} ({rows} rows x 128 heads), fp64 numpy, {t:.1f} s"}
+
+
+def oracle_config5(x, budget_s=4.0):
+    """The fp64 oracle of the long causal fp8 prefill for q/kv head 0: RoPE
+    and per-head fp8 quantization first (not timed), then chunks of 256 query
+    rows drawn at random from the 32768 until the budget is spent; TFLOP/s
+    counts the visible (query, key) pairs of the rows done."""
+    from oracle.attention import dequant_fp8_per_head, prefill_varlen
+    from oracle.quant import quant_fp8_per_head
+    from oracle.rope import append_kv_rope
+    S, ps = 32768, x["page_size"]
+    one = lambda a: np.ascontiguousarray(a[:, :1])
+    tp = time.perf_counter()
+    zero = np.zeros((x["num_pages"], ps, 1, 128), np.uint16)
+    ref = append_kv_rope(one(x["q"]), one(x["k"]), one(x["v"]), "bf16", x["cu_seqlens"], x["kv_len_before"],
+                         x["rope_cos_sin"], zero, zero.copy(), x["kv_indptr"], x["kv_indices"], ps)
+    qd = dequant_fp8_per_head(*quant_fp8_per_head(ref[0], "bf16"))
+    kd = dequant_fp8_per_head(*quant_fp8_per_head(ref[1], "bf16"))
+    vd = dequant_fp8_per_head(*quant_fp8_per_head(one(x["v"]), "bf16"))
+    t_prep = time.perf_counter() - tp
+    cu = np.array([0, S], np.int32)
+    rng = np.random.default_rng(55)
+    t, pairs, chunks = 0.0, 0, 0
+    for c in rng.permutation(S // 256):
+        if t >= budget_s:
+            break
+        idx = np.arange(c * 256, (c + 1) * 256)
+        t0 = time.perf_counter()
+        prefill_varlen(qd, kd, vd, cu, cu, x["sm_scale"], True, "bf16", rows=[(0, 0, idx)])
+        t += time.perf_counter() - t0
+        pairs += int((idx + 1).sum())
+        chunks += 1
+    return {"TFLOP/s": 4.0 * 128 * pairs / t / 1e12, "cores": host_cores(), "kind": "oracle",
+            "sample": f"head 0, {chunks} random chunks of 256 query rows ({pairs} causal pairs), fp64 numpy, "
+                      f"{t:.1f} s (RoPE + quantization {t_prep:.1f} s not counted)"}
 
 
 def kernel_source_hash() -> str:
@@ -328,11 +416,7 @@ def cpu_baseline(x, budget_s=12.0):
     the time budget is spent."""
     from oracle.attention import dequant_int8_per_block, prefill_varlen
     from oracle.quant import quant_int8_per_block, as_f32
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = host_cores()
     cu = x["cu_seqlens"]
     t_att, t_prep, flops, done = 0.0, 0.0, 0.0, []
     for b in range(len(cu) - 1):
@@ -405,7 +489,8 @@ def main():
             continue
         log(f"[bench] {name}")
         try:
-            extra[{"c3": "config3_decode", "c5": "config5_long_prefill", "c4": "config4_sparse_mla"}[name]] = fn(it)
+            extra[{"c3": "config3_decode", "c5": "config5_long_prefill", "c4": "config4_sparse_mla"}[name]] = \
+                fn(it, cpu=not a.no_cpu_baseline)
         except Exception as ex:  # report, keep the headline line
             extra[name] = {"error": f"{type(ex).__name__}: {ex}"}
         torch.cuda.empty_cache()
