@@ -346,8 +346,8 @@ int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* b
   a.block_size = block_size; a.max_blocks = max_blocks_per_seq; a.topk = topk;
   a.n_split = attnq::mla_n_split(topk);
   const size_t rows = (size_t)batch * s_q * a.n_split * num_heads;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = a.ws_o + rows * 512;
+  a.ws_o = static_cast<uint16_t*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(a.ws_o + rows * 512);
   a.sm_scale_log2 = sm_scale * LOG2E;
   LAUNCHED(attnq::launch_mla(a, stream));
   return ok();

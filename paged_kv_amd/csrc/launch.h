@@ -79,7 +79,7 @@ struct MlaArgs {
   const int32_t* block_table;
   const int32_t* kv_lens;
   const int32_t* idx;      // [B, Sq, 1, topk]
-  float* ws_o;             // [B*Sq, n_split, H, 512]
+  uint16_t* ws_o;          // bf16 [B*Sq, n_split, H, 512]
   float* ws_lse;           // [B*Sq, n_split, H]
   void* o;
   float* lse;

@@ -19,11 +19,12 @@
 //   softmax per head against a lagging reference max (exact rescale only
 //   when a step's fp16 row sum leaves range), lane-local partial sums;
 //   O^T += codes^T (P * scale_t)^T   fp16 MFMA, one P operand per tile.
-// Each split writes its normalized partial O and log2-sum-exp; the merge
-// kernel combines the splits.
+// Each split writes its normalized partial O (bf16) and log2-sum-exp; the
+// merge kernel combines the splits.
 //
 // The query's nope part is rounded to fp16 for the fp16 MFMA (exact for
-// 2^-14 <= |q| <= 65504); everything else is exact up to fp32 accumulation.
+// 2^-14 <= |q| <= 65504) and the split partials of O are stored in bf16;
+// everything else is exact up to fp32 accumulation.
 #include "kcommon.h"
 #include "launch.h"
 
@@ -317,7 +318,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const v4f o4 = oacc[db] * inv;
-      *reinterpret_cast<v4f*>(a.ws_o + prow * MLA_NOPE + 128 * t + db * 16 + 4 * g) = o4;
+      const uint32_t w0 = f32_to_bf16(o4[0]) | (f32_to_bf16(o4[1]) << 16);
+      const uint32_t w1 = f32_to_bf16(o4[2]) | (f32_to_bf16(o4[3]) << 16);
+      *reinterpret_cast<uint2*>(a.ws_o + prow * MLA_NOPE + 128 * t + db * 16 + 4 * g) = make_uint2(w0, w1);
     }
     if (g == 0 && t == 0) a.ws_lse[prow] = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
   }
@@ -339,8 +342,9 @@ __global__ __launch_bounds__(128) void k_mla_merge(const MlaArgs a) {
       if (lc == -INFINITY) continue;
       const float w = __builtin_amdgcn_exp2f(lc - m);
       tot += w;
-      const float4 o4 = *reinterpret_cast<const float4*>(a.ws_o + prow * MLA_NOPE + d0);
-      acc[0] += w * o4.x; acc[1] += w * o4.y; acc[2] += w * o4.z; acc[3] += w * o4.w;
+      const uint2 o2 = *reinterpret_cast<const uint2*>(a.ws_o + prow * MLA_NOPE + d0);
+      acc[0] += w * bf16_to_f32(o2.x & 0xffffu); acc[1] += w * bf16_to_f32(o2.x >> 16);
+      acc[2] += w * bf16_to_f32(o2.y & 0xffffu); acc[3] += w * bf16_to_f32(o2.y >> 16);
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
@@ -354,7 +358,7 @@ int mla_n_split(int topk) { return (topk + MLA_SPLIT_TOKENS - 1) / MLA_SPLIT_TOK
 
 size_t mla_workspace_bytes(int batch, int s_q, int heads, int topk) {
   const size_t rows = (size_t)batch * s_q * mla_n_split(topk) * heads;
-  return rows * MLA_NOPE * sizeof(float) + rows * sizeof(float) + 256;
+  return rows * MLA_NOPE * sizeof(uint16_t) + rows * sizeof(float) + 256;
 }
 
 bool launch_mla(const MlaArgs& a, hipStream_t s) {
