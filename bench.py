@@ -10,7 +10,9 @@ TFLOP/s (4 * D * H_q * sum over sequences of L(L+1)/2).
 
 Also reported (``extra``): the paged fp8 decode (GB/s of K/V bytes), the
 long fp8 prefill with RoPE + paged append (TFLOP/s), the sparse MLA decode
-(GB/s) when available, each timed on its own.
+(GB/s) and a chunked prefill against a paged bf16 cache (TFLOP/s of the
+prefill alone and of page gather + quantization + prefill), each timed on
+its own, each with the oracle timed beside it on a bounded sample.
 
 ``roofline``: the prefill kernel alone, timed with HIP events on the stream
 it is launched on, against the MFMA peak of its two contractions (int8 QK at
@@ -226,6 +228,71 @@ def bench_config4(iters, cpu=False):
     if cpu:
         r["cpu_oracle"] = oracle_config4(x)
     return r
+
+
+def bench_paged_prefill(iters, cpu=False):
+    """Chunked prefill against the paged bf16 cache: gather + fp8 quant + prefill."""
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import PagedPrefill
+    from tests.parity import to_dev
+    x = gen.paged_prefill_workload()
+    p = PagedPrefill(to_dev(x["q"]), to_dev(x["k_cache"]), to_dev(x["v_cache"]), to_dev(x["kv_indptr"]),
+                     to_dev(x["kv_indices"]), to_dev(x["kv_last_page_len"]), to_dev(x["cu_q"]),
+                     to_dev(x["cu_k"]), x["max_q"], x["max_k"], x["sm_scale"], causal=True)
+    p.run()
+    torch.cuda.synchronize()
+    lq, lk = x["q_lens"].astype(np.int64), x["kv_lens"].astype(np.int64)
+    pairs = float(np.sum(lq * (lk - lq) + lq * (lq + 1) // 2))
+    flops = 4.0 * 128 * 32 * pairs
+    settle(p.attend)
+    kms = time_events(p.attend, iters)
+    pipe = time_events(p.run, max(2, iters // 2))
+    med = float(np.median(kms))
+    r = {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
+         "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
+         "pipeline_ms": float(np.median(pipe)),
+         "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12,
+         "gathered_bytes": float(2 * np.sum(lk) * 8 * 128 * 2)}
+    if cpu:
+        r["cpu_oracle"] = oracle_paged_prefill(x)
+    return r
+
+
+def oracle_paged_prefill(x, budget_s=4.0):
+    """The fp64 oracle of the chunked paged prefill: pages read into the
+    ragged layout and fp8 quantization first (not timed), then whole
+    (sequence, q head) problems in order, in blocks of 256 query rows, until
+    the budget is spent; TFLOP/s counts the visible (query, key) pairs done."""
+    from oracle.attention import dequant_fp8_per_head, prefill_varlen, ragged_from_pages
+    from oracle.quant import quant_fp8_per_head
+    tp = time.perf_counter()
+    kg = ragged_from_pages(x["k_cache"], x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], x["cu_k"])
+    vg = ragged_from_pages(x["v_cache"], x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], x["cu_k"])
+    qd = dequant_fp8_per_head(*quant_fp8_per_head(x["q"], "bf16"))
+    kd = dequant_fp8_per_head(*quant_fp8_per_head(kg, "bf16"))
+    vd = dequant_fp8_per_head(*quant_fp8_per_head(vg, "bf16"))
+    t_prep = time.perf_counter() - tp
+    t, pairs, chunks, done = 0.0, 0, 0, []
+    for b in range(len(x["q_lens"])):
+        lq, lk = int(x["q_lens"][b]), int(x["kv_lens"][b])
+        h = 0
+        while h < 32 and t < budget_s:
+            for c in range(lq // 256):
+                idx = np.arange(c * 256, (c + 1) * 256)
+                t0 = time.perf_counter()
+                prefill_varlen(qd, kd, vd, x["cu_q"], x["cu_k"], x["sm_scale"], True, "bf16", rows=[(b, h, idx)])
+                t += time.perf_counter() - t0
+                pairs += int((idx + lk - lq + 1).sum())
+                chunks += 1
+            h += 1
+        done.append(f"{b}:{h}h")
+        if t >= budget_s:
+            break
+    return {"TFLOP/s": 4.0 * 128 * pairs / t / 1e12, "cores": host_cores(), "kind": "oracle",
+            "sample": f"whole (sequence, q head) chunks ({' '.join(done)}; {chunks} blocks of 256 query rows, "
+                      f"{pairs} causal pairs), fp64 numpy, {t:.1f} s (page reads + quantization "
+                      f"{t_prep:.1f} s not counted)"}
 
 
 def host_cores() -> int:
@@ -451,7 +518,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--extra", default="c3,c5,c4", help="comma list of extra workloads (c3,c4,c5) or ''")
+    ap.add_argument("--extra", default="c3,c5,c4,paged", help="comma list of extra workloads (c3,c4,c5,paged) or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the calibration copy and one prefill launch (for rocprofv3 --pmc)")
@@ -484,12 +551,14 @@ def main():
                          "untimed_settle_ms": r2["settle_ms"],
                          "prefill_kernel_TFLOPS": k_tflops, "pct_fp8_peak_step": 100 * value / PEAK_FP8,
                          "pct_fp8_peak_kernel": 100 * k_tflops / PEAK_FP8}}
-    for name, fn, it in (("c3", bench_config3, 20), ("c5", bench_config5, 5), ("c4", bench_config4, 30)):
+    for name, fn, it in (("c3", bench_config3, 20), ("c5", bench_config5, 5), ("c4", bench_config4, 30),
+                         ("paged", bench_paged_prefill, 10)):
         if name not in a.extra.split(","):
             continue
         log(f"[bench] {name}")
         try:
-            extra[{"c3": "config3_decode", "c5": "config5_long_prefill", "c4": "config4_sparse_mla"}[name]] = \
+            extra[{"c3": "config3_decode", "c5": "config5_long_prefill", "c4": "config4_sparse_mla",
+                   "paged": "chunked_prefill_paged"}[name]] = \
                 fn(it, cpu=not a.no_cpu_baseline)
         except Exception as ex:  # report, keep the headline line
             extra[name] = {"error": f"{type(ex).__name__}: {ex}"}

@@ -30,6 +30,7 @@ __all__ = [
     "paged_decode_inputs", "config3",
     "sparse_mla_inputs", "config4",
     "long_prefill_inputs", "config5", "rope_cos_sin_table",
+    "paged_prefill_inputs", "paged_prefill_workload", "paged_prefill_workload_lengths",
     "MLA_ROW_BYTES", "MLA_NOPE", "MLA_ROPE", "MLA_TILE",
 ]
 
@@ -359,4 +360,68 @@ def sparse_mla_inputs(seed: int, batch: int, s_q: int, heads: int, kv_len,
 def config4() -> dict:
     x = sparse_mla_inputs(seed_for(4), 32, 1, 128, 65536, 64, 2048)
     x.update(sm_scale=1.0 / 24.0, name="c4_sparse_mla_int8")
+    return x
+
+
+# ---------------------------------------------------------------------------
+# prefill chunk against a paged 16-bit cache (the paged prefill run mode)
+# ---------------------------------------------------------------------------
+def paged_prefill_inputs(seed: int, kv_lens, q_lens, hq: int, hkv: int, d: int,
+                         page_size: int = 64, spare_frac: float = 0.05) -> dict:
+    """A prefill chunk whose queries are the last q_lens[b] of kv_lens[b]
+    tokens of sequence b, against bf16 K/V page pools [num_pages, page_size,
+    hkv, d] (NHD) that already hold all kv_lens[b] tokens (the chunk's own
+    keys included, as after the append step).  q: bf16 N(0,1) [sum q_lens,
+    hq, d]; K and V: bf16 N(0,1).  Pages of all sequences are a random
+    permutation of the pool; spare pages and the unused slots of each last
+    page hold the bf16 NaN 0x7FC0, which must never reach an output.
+    cu_q / cu_k are the ragged row offsets of the queries and of the keys."""
+    rng = np.random.default_rng(seed)
+    kv_lens = np.asarray(kv_lens, np.int64)
+    q_lens = np.asarray(q_lens, np.int64)
+    assert kv_lens.shape == q_lens.shape and np.all(q_lens <= kv_lens)
+    b = kv_lens.size
+    npages = (kv_lens + page_size - 1) // page_size
+    used = int(npages.sum())
+    pool = used + int(math.ceil(spare_frac * used))
+    perm = rng.permutation(pool).astype(np.int32)
+    indptr = _cu(npages)
+    last = np.where(kv_lens > 0, kv_lens - (npages - 1) * page_size, 0).astype(np.int32)
+    q = bf16_bits(_normal_f32(rng, (int(q_lens.sum()), hq, d)))
+    caches = {}
+    for name in ("k_cache", "v_cache"):
+        c = np.full((pool, page_size, hkv, d), 0x7FC0, np.uint16)
+        for i in range(b):
+            n = int(kv_lens[i])
+            if n == 0:
+                continue
+            rows = bf16_bits(_normal_f32(rng, (n, hkv, d)))
+            pages = perm[indptr[i]:indptr[i + 1]]
+            for j, pg in enumerate(pages):
+                s0 = j * page_size
+                m = min(page_size, n - s0)
+                c[pg, :m] = rows[s0:s0 + m]
+        caches[name] = c
+    return {
+        "q": q, "k_cache": caches["k_cache"], "v_cache": caches["v_cache"],
+        "kv_indptr": indptr, "kv_indices": perm[:used].copy(), "kv_last_page_len": last,
+        "kv_lens": kv_lens.astype(np.int32), "q_lens": q_lens.astype(np.int32),
+        "cu_q": _cu(q_lens), "cu_k": _cu(kv_lens),
+        "num_pages": pool, "page_size": page_size, "hq": hq, "hkv": hkv, "d": d,
+        "max_q": int(q_lens.max()) if b else 0, "max_k": int(kv_lens.max()) if b else 0,
+    }
+
+
+def paged_prefill_workload_lengths(seed: int = None, batch: int = 4):
+    rng = np.random.default_rng(seed_for(6) if seed is None else seed)
+    return rng.integers(8192, 24577, size=batch).astype(np.int32)
+
+
+def paged_prefill_workload() -> dict:
+    """Chunked prefill against a paged bf16 cache: B=4 sequences of kv_len
+    U{8192..24576} (seeded) whose last 2048 tokens are the new chunk, 32 q /
+    8 kv heads, D=128, page size 64, causal."""
+    kv = paged_prefill_workload_lengths()
+    x = paged_prefill_inputs(seed_for(6) + 1, kv, np.full(kv.size, 2048), 32, 8, 128, 64)
+    x.update(sm_scale=1.0 / math.sqrt(128.0), name="chunked_prefill_paged_bf16")
     return x

@@ -176,6 +176,30 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
                         int o_dtype, float* lse, hipStream_t stream);
 
 /*
+ * attn_gather_paged_kv -- reads a paged KV cache into the ragged contiguous
+ * layout [total_k, num_kv_heads, head_dim], so that a prefill chunk can attend
+ * to the tokens already in the cache (FlashInfer's prefill run against a paged
+ * KV cache; the pages as FlashInfer and attn_append_kv_rope lay them out).
+ *   cache [num_pages, page_size, num_kv_heads, head_dim] (NHD), elem_bytes 1
+ *   (fp8 / int8 codes) or 2 (bf16 / fp16); the bytes are copied unchanged.
+ *   kv_indptr [batch+1], kv_indices [kv_indptr[batch]], kv_last_page_len [batch]:
+ *   sequence b holds kv_len[b] = (kv_indptr[b+1]-kv_indptr[b]-1)*page_size +
+ *   kv_last_page_len[b] tokens (0 with no page); token i is slot i % page_size of
+ *   page kv_indices[kv_indptr[b] + i / page_size].
+ *   cu_seqlens_k [batch+1] (device): row cu_seqlens_k[b] + i of out receives token i,
+ *   for i < cu_seqlens_k[b+1] - cu_seqlens_k[b]; rows past kv_len[b], and rows whose
+ *   page index lies outside [0, num_pages), are zero-filled.  max_seqlen_k must be
+ *   >= every cu_seqlens_k[b+1] - cu_seqlens_k[b] (rows beyond it are not written).
+ *   out [cu_seqlens_k[batch], num_kv_heads, head_dim], caller-allocated.
+ *   head_dim in {64, 128}.  All pointers are device pointers; nothing is allocated.
+ */
+int attn_gather_paged_kv(const void* cache, int elem_bytes, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                         const int32_t* cu_seqlens_k, int batch, int max_seqlen_k, int num_pages,
+                         int page_size, int num_kv_heads, int head_dim, void* out,
+                         hipStream_t stream);
+
+/*
  * attn_decode_paged -- one query token per sequence against a paged fp8 cache,
  * split over KV chunks and merged by log-sum-exp (FlashInfer
  * BatchDecodeWithPagedKVCachePlan/Run; aiter's paged fp8 flash_attn_with_kvcache).

@@ -176,6 +176,25 @@ def gather_pages(cache: np.ndarray, kv_indptr, kv_indices, b: int, kv_len: int) 
     return cache[pages, t % ps]
 
 
+def ragged_from_pages(cache: np.ndarray, kv_indptr, kv_indices, kv_last_page_len, cu_k) -> np.ndarray:
+    """The paged cache read into the ragged layout a prefill attends to
+    (FlashInfer's prefill against a paged KV cache: the pages hold each
+    sequence's tokens in order, page kv_indices[kv_indptr[b] + i // page_size],
+    slot i % page_size).  Row cu_k[b] + i is token i of sequence b for
+    i < min(kv_len[b], cu_k[b+1] - cu_k[b]); rows past kv_len[b] are zero.
+    cache [P, page_size, H, D] of any dtype -> [cu_k[-1], H, D]."""
+    cu_k = np.asarray(cu_k, np.int64)
+    ps = cache.shape[1]
+    lens = paged_kv_len(kv_indptr, kv_last_page_len, ps)
+    out = np.zeros((int(cu_k[-1]),) + cache.shape[2:], cache.dtype)
+    for b in range(len(cu_k) - 1):
+        n = int(cu_k[b + 1] - cu_k[b])
+        m = min(n, int(lens[b]))
+        if m > 0:
+            out[cu_k[b]:cu_k[b] + m] = gather_pages(cache, kv_indptr, kv_indices, b, m)
+    return out
+
+
 def decode_paged(q_bits, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices,
                  kv_last_page_len, sm_scale, batches=None):
     """q bf16 bits [B, Hq, D]; fp8 caches [P, page_size, Hkv, D]; descales [Hkv].

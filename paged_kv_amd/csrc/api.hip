@@ -8,6 +8,7 @@
 
 #include "../../include/attnq.h"
 #include "launch.h"
+#include "gather.h"
 
 namespace {
 
@@ -244,6 +245,36 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
                    : qk_dtype == ATTNQ_BF16 ? attnq::PF_Q_RAW_BF16 : attnq::PF_Q_RAW_F16;
   LAUNCHED(attnq::launch_prefill(a, head_dim, q_mode, v_dtype == ATTNQ_FP8E4M3, o_dtype == ATTNQ_BF16,
                                  max_seqlen_q, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_gather_paged_kv
+int attn_gather_paged_kv(const void* cache, int elem_bytes, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                         const int32_t* cu_seqlens_k, int batch, int max_seqlen_k, int num_pages,
+                         int page_size, int num_kv_heads, int head_dim, void* out,
+                         hipStream_t stream) {
+  REQUIRE(elem_bytes == 1 || elem_bytes == 2, ATTNQ_EINVAL, "elem_bytes must be 1 or 2 (got %d)", elem_bytes);
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_kv_heads > 0 && num_pages > 0 && page_size > 0, ATTNQ_EINVAL,
+          "num_kv_heads, num_pages and page_size must be positive");
+  REQUIRE(batch >= 0 && max_seqlen_k >= 0, ATTNQ_EINVAL, "batch and max_seqlen_k must be >= 0");
+  if (batch == 0 || max_seqlen_k == 0) return ok();
+  REQUIRE((long)num_kv_heads * head_dim * elem_bytes < (1L << 20), ATTNQ_EUNSUPPORTED, "row too wide");
+  REQUIRE_PTR(cache, 16);
+  REQUIRE_PTR(kv_indptr, 4);
+  REQUIRE_PTR(kv_indices, 4);
+  REQUIRE_PTR(kv_last_page_len, 4);
+  REQUIRE_PTR(cu_seqlens_k, 4);
+  REQUIRE_PTR(out, 16);
+  attnq::GatherArgs a;
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.kv_indptr = kv_indptr; a.kv_indices = kv_indices; a.kv_last_page_len = kv_last_page_len;
+  a.cu_k = cu_seqlens_k;
+  a.out = static_cast<uint8_t*>(out);
+  a.batch = batch; a.num_pages = num_pages; a.page_size = page_size;
+  a.row_bytes = num_kv_heads * head_dim * elem_bytes;
+  LAUNCHED(attnq::launch_gather_paged(a, max_seqlen_k, stream));
   return ok();
 }
 

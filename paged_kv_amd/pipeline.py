@@ -162,6 +162,66 @@ class AppendRopeFp8Prefill:
         return self.prefill.run()
 
 
+class PagedPrefill:
+    """A prefill chunk against a paged 16-bit KV cache (FlashInfer's paged
+    prefill run): the sequences' pages are read into the ragged layout
+    (attn_gather_paged_kv), then Q (the chunk), K and V (the gathered cache)
+    get fp8 per-head quantization (V permuted, each code stored as its exact
+    fp16 value) and the varlen prefill runs with cu_seqlens_q != cu_seqlens_k,
+    the chunk's queries aligned to the end of their sequence's keys."""
+
+    def __init__(self, q, k_cache, v_cache, kv_indptr, kv_indices, kv_last_page_len, cu_q, cu_k,
+                 max_q, max_k, sm_scale, causal=True, out_dtype=torch.bfloat16, want_lse=False):
+        dev = q.device
+        if k_cache.dtype not in (torch.bfloat16, torch.float16) or v_cache.dtype != k_cache.dtype:
+            raise TypeError("PagedPrefill takes bf16 or fp16 caches of one dtype")
+        self.q, self.kc_pages, self.vc_pages = q, k_cache, v_cache
+        self.ip, self.ix, self.lpl, self.cu_q, self.cu_k = kv_indptr, kv_indices, kv_last_page_len, cu_q, cu_k
+        self.tq, self.hq, self.d = q.shape
+        self.num_pages, self.page_size, self.hkv, _ = k_cache.shape
+        self.b = cu_q.numel() - 1
+        self.max_q, self.max_k = int(max_q), int(max_k)
+        self.tk = int(cu_k[-1].item())
+        self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        self.kg = torch.empty((self.tk, self.hkv, self.d), dtype=k_cache.dtype, device=dev)
+        self.vg = torch.empty_like(self.kg)
+        self.qc = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        self.kc = torch.empty(self.kg.shape, dtype=torch.uint8, device=dev)
+        self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_k, 128)), dtype=torch.float16,
+                              device=dev)
+        self.qs = torch.empty(self.hq, dtype=torch.float32, device=dev)
+        self.ks = torch.empty(self.hkv, dtype=torch.float32, device=dev)
+        self.vs = torch.empty(self.hkv, dtype=torch.float32, device=dev)
+        self.o = torch.empty((self.tq, self.hq, self.d), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((self.hq, self.tq), dtype=torch.float32, device=dev) if want_lse else None
+
+    def gather(self):
+        for pages, out in ((self.kc_pages, self.kg), (self.vc_pages, self.vg)):
+            A.attn_gather_paged_kv(pages, 2, self.ip, self.ix, self.lpl, self.cu_k, self.b, self.max_k,
+                                   self.num_pages, self.page_size, self.hkv, self.d, out)
+
+    def quantize(self):
+        dq, dk = _dtype_code(self.q), _dtype_code(self.kg)
+        A.attn_quant_qk(self.q, dq, self.cu_q, self.b, self.max_q, self.tq, self.hq, self.d,
+                        A.Q_FP8_PER_HEAD, 128, None, self.qc, self.qs)
+        A.attn_quant_qk(self.kg, dk, self.cu_k, self.b, self.max_k, self.tk, self.hkv, self.d,
+                        A.Q_FP8_PER_HEAD, 128, None, self.kc, self.ks)
+        A.attn_quant_v_permute(self.vg, dk, self.cu_k, self.b, self.max_k, self.tk, self.hkv, self.d,
+                               A.Q_FP8_PER_HEAD_WIDE, None, self.vp, self.vs)
+
+    def attend(self):
+        A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3, A.FP16, self.qs, self.ks, self.vs,
+                              A.Q_FP8_PER_HEAD, self.cu_q, self.cu_k, self.b, self.max_q, self.max_k,
+                              self.tq, self.tk, self.hq, self.hkv, self.d, self.sm_scale, self.causal,
+                              self.o, _dtype_code(self.o), self.lse)
+
+    def run(self):
+        self.gather()
+        self.quantize()
+        self.attend()
+        return self.o
+
+
 class PagedDecode:
     """Split-KV paged fp8 decode + log-sum-exp merge."""
 

@@ -21,10 +21,10 @@ def _declared():
     return re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(\w+)\s*\(", src, flags=re.M)
 
 
-def test_header_declares_the_six_calls():
+def test_header_declares_the_calls():
     names = set(_declared())
     for n in ["attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
-              "attn_decode_paged", "attn_sparse_mla_decode"]:
+              "attn_gather_paged_kv", "attn_decode_paged", "attn_sparse_mla_decode"]:
         assert n in names
 
 
@@ -131,6 +131,25 @@ def test_decode_validation():
     assert need > 0
     assert _decode(wsb=need - 1) == -3
     assert _decode(ws=FAKE + 8) == -1
+
+
+def _gather(**kw):
+    a = dict(c=FAKE, eb=2, ip=FAKE, ix=FAKE, lpl=FAKE, cu=FAKE, b=2, mk=100, np_=64, ps=16, hkv=8,
+             d=128, out=FAKE, st=None)
+    a.update(kw)
+    return pk.lib().attn_gather_paged_kv(*a.values())
+
+
+def test_gather_validation():
+    assert _gather(eb=4) == -1 and "elem_bytes" in _err()
+    assert _gather(d=96) == -2 and "head_dim" in _err()
+    assert _gather(ps=0) == -1
+    assert _gather(np_=0) == -1
+    assert _gather(b=-1) == -1
+    assert _gather(out=FAKE + 4) == -1 and "aligned" in _err()
+    assert _gather(cu=None) == -1 and "cu_seqlens_k" in _err()
+    assert _gather(b=0, c=None) == 0          # nothing to do: no pointer is needed
+    assert _gather(mk=0, c=None) == 0
 
 
 def _mla(**kw):

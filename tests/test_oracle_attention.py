@@ -276,3 +276,56 @@ def test_mla_unit_scales_zero_rope_is_plain_int8_attention():
     p = np.exp(lg - lg.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     assert np.allclose(r["o_exact"][0, 0], p @ codes, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# reading the paged cache into the ragged layout (prefill against pages)
+# ---------------------------------------------------------------------------
+def _page_walk(cache, kv_indptr, kv_indices, kv_last_page_len, b):
+    """Tokens of sequence b by walking its pages in order, slot by slot."""
+    ps = cache.shape[1]
+    pages = list(kv_indices[kv_indptr[b]:kv_indptr[b + 1]])
+    rows = []
+    for j, pg in enumerate(pages):
+        m = ps if j < len(pages) - 1 else int(kv_last_page_len[b])
+        for s in range(m):
+            rows.append(cache[pg, s])
+    return np.array(rows, cache.dtype).reshape((-1,) + cache.shape[2:])
+
+
+def test_ragged_from_pages_vs_page_walk():
+    from oracle.attention import ragged_from_pages
+    x = gen.paged_prefill_inputs(21, [5, 0, 9, 13], [2, 0, 9, 1], 2, 2, 8, page_size=4, spare_frac=0.5)
+    for name in ("k_cache", "v_cache"):
+        got = ragged_from_pages(x[name], x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], x["cu_k"])
+        cu = x["cu_k"]
+        for b in range(4):
+            ref = _page_walk(x[name], x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], b)
+            assert np.array_equal(got[cu[b]:cu[b + 1]], ref)
+        assert not np.any(got == 0x7FC0)  # no spare page or unused slot leaks in
+
+
+def test_ragged_from_pages_rows_past_the_cache_are_zero():
+    from oracle.attention import ragged_from_pages
+    x = gen.paged_prefill_inputs(22, [6, 3], [1, 1], 1, 1, 4, page_size=4)
+    cu = np.array([0, 8, 12], np.int32)  # 2 and 1 rows more than cached
+    got = ragged_from_pages(x["k_cache"], x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], cu)
+    assert np.array_equal(got[0:6], _page_walk(x["k_cache"], x["kv_indptr"], x["kv_indices"],
+                                               x["kv_last_page_len"], 0))
+    assert not got[6:8].any() and not got[11:12].any()
+
+
+def test_ragged_from_pages_returns_what_the_append_wrote():
+    from oracle.attention import ragged_from_pages
+    from oracle.rope import append_kv_rope
+    x = gen.long_prefill_inputs(23, [7, 5, 12], 2, 2, 8, 4)
+    shape = (x["num_pages"], 4, 2, 8)
+    kc = np.full(shape, 0x7FC0, np.uint16)
+    vc = np.full(shape, 0x7FC0, np.uint16)
+    q_rot, k_rot, kc2, vc2 = append_kv_rope(x["q"], x["k"], x["v"], "bf16", x["cu_seqlens"], x["kv_len_before"],
+                                            x["rope_cos_sin"], kc, vc, x["kv_indptr"], x["kv_indices"], 4)[:4]
+    lens = np.diff(x["cu_seqlens"]) + x["kv_len_before"]
+    npg = np.diff(x["kv_indptr"])
+    last = (lens - (npg - 1) * 4).astype(np.int32)
+    assert np.array_equal(ragged_from_pages(kc2, x["kv_indptr"], x["kv_indices"], last, x["cu_seqlens"]), k_rot)
+    assert np.array_equal(ragged_from_pages(vc2, x["kv_indptr"], x["kv_indices"], last, x["cu_seqlens"]), x["v"])
