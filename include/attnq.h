@@ -176,6 +176,27 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
                         int o_dtype, float* lse, hipStream_t stream);
 
 /*
+ * attn_smooth_quant_k -- SageAttention's smoothing of K before its int8
+ * quantization (PaddleNLP "Sage Attention Support Varlen" and SageAttention:
+ * subtracting a per-channel mean from K changes every logit of a query by
+ * the same amount, so the softmax output is unchanged while the channel
+ * offsets stop inflating the int8 block scales).
+ *   k fp16 [total_tokens, num_kv_heads, head_dim], cu_seqlens [batch+1] (device).
+ *   mean fp32 [batch, num_kv_heads, head_dim] (written): the mean of each channel
+ *   over the sequence's tokens, fp32(fp64(S) / fp64(L)) with S the exact sum; 0
+ *   for an empty sequence.
+ *   codes int8 [total_tokens, num_kv_heads, head_dim] and scales fp32
+ *   [batch, num_kv_heads, ceil(max_seqlen/128)]: attn_quant_qk's INT8_PER_BLOCK
+ *   applied to k - mean (one fp32 subtraction per element).
+ *   With these codes attn_prefill_varlen returns the same softmax output; its
+ *   lse is that of the smoothed logits, i.e. lower by sm_scale * q . mean for
+ *   each query.  block_tokens must be 128; head_dim in {64, 128}.
+ */
+int attn_smooth_quant_k(const void* k, const int32_t* cu_seqlens, int batch, int max_seqlen,
+                        int total_tokens, int num_kv_heads, int head_dim, int block_tokens,
+                        void* codes, float* scales, float* mean, hipStream_t stream);
+
+/*
  * attn_gather_paged_kv -- reads a paged KV cache into the ragged contiguous
  * layout [total_k, num_kv_heads, head_dim], so that a prefill chunk can attend
  * to the tokens already in the cache (FlashInfer's prefill run against a paged

@@ -21,10 +21,19 @@ Token permutation pi inside a 32-token group (j in [0, 32)):
     half = j // 16, g = (j % 16) // 4, r = j % 4  ->  pi(j) = 8 g + 4 half + r
 so stored position p = 8 g + s holds token (s // 4) * 16 + 4 g + s % 4.
 
+* ``channel_mean_fp16`` / ``smooth_quant_k`` -- SageAttention's K smoothing
+  before the int8 block quantization: subtract each sequence's per-channel
+  mean of K (softmax-invariant).  Reading: exact sum, mean = fp32(fp64(S)/L),
+  then codes of fp32(k) - mean.
+
 Pins (tests/test_oracle_quant.py): amax and descale by exhaustive
 comparison with a per-element Python max; codes against the brute-force
 nearest-grid encoder; block boundaries at sequence starts; pi is a
-bijection and its inverse recovers V bit-exactly; padding is +0.
+bijection and its inverse recovers V bit-exactly; padding is +0; the
+channel mean against exact rational arithmetic, its independence of token
+order and its exactness on constant channels; smoothing leaves fp64 attention
+unchanged (test_oracle_attention.py) and shrinks the int8 error of K on data
+with channel offsets.
 """
 from __future__ import annotations
 
@@ -36,11 +45,13 @@ PERM_GROUP = 32
 
 
 def as_f32(x: np.ndarray, dtype: str) -> np.ndarray:
-    """bf16 bits (uint16) or fp16 array -> exact fp32 values."""
+    """bf16 bits (uint16) or fp16 array -> exact fp32 values ("f32": x as is)."""
     if dtype == "bf16":
         return bf16_bits_to_f32(x)
     if dtype == "fp16":
         return np.asarray(x, dtype=np.float16).astype(np.float32)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
     raise ValueError(dtype)
 
 
@@ -150,3 +161,33 @@ def v_unpermute(v_out: np.ndarray, seqlens) -> list:
     for bi, n in enumerate(seqlens):
         res.append(np.transpose(v_out[bi][:, :, pos_of[:int(n)]], (2, 0, 1)))
     return res
+
+
+def channel_mean_fp16(x: np.ndarray, cu_seqlens) -> np.ndarray:
+    """Per-sequence, per-channel mean of fp16 x [T, H, D] -> fp32 [B, H, D]
+    (SageAttention's K smoothing; PaddleNLP "Sage Attention Support Varlen").
+    Reading: the sum S over the sequence's tokens is exact (every fp16 value
+    is an integer number of 2^-24 units; the units are summed as integers),
+    then mean = fp32(fp64(S) / fp64(L)); 0 for an empty sequence."""
+    units = (np.asarray(x, np.float16).astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    cu = np.asarray(cu_seqlens, np.int64)
+    b = len(cu) - 1
+    out = np.zeros((b,) + units.shape[1:], np.float32)
+    for i in range(b):
+        s0, s1 = int(cu[i]), int(cu[i + 1])
+        if s1 > s0:
+            tot = units[s0:s1].sum(axis=0, dtype=np.int64)
+            out[i] = (tot.astype(np.float64) / np.float64(s1 - s0)).astype(np.float32) * np.float32(2.0 ** -24)
+    return out
+
+
+def smooth_quant_k(k: np.ndarray, cu_seqlens, max_seqlen: int, block_tokens: int = 128):
+    """K smoothing then int8 per block: codes and scales of fp32(k) - mean
+    (one fp32 subtraction per element), and the means."""
+    mean = channel_mean_fp16(k, cu_seqlens)
+    k32 = as_f32(k, "fp16").copy()
+    cu = np.asarray(cu_seqlens, np.int64)
+    for i in range(len(cu) - 1):
+        k32[cu[i]:cu[i + 1]] = k32[cu[i]:cu[i + 1]] - mean[i][None]
+    codes, scales = quant_int8_per_block(k32, "f32", cu_seqlens, max_seqlen, block_tokens)
+    return codes, scales, mean

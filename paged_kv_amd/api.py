@@ -17,7 +17,8 @@ __all__ = [
     "Q_INT8_PER_BLOCK_RAW_Q",
     "library_path", "lib", "abi_version",
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
-    "attn_gather_paged_kv", "attn_decode_paged_workspace_size", "attn_decode_paged",
+    "attn_smooth_quant_k", "attn_gather_paged_kv", "attn_decode_paged_workspace_size",
+    "attn_decode_paged",
     "attn_sparse_mla_decode_workspace_size", "attn_sparse_mla_decode",
     "SYMBOLS",
 ]
@@ -40,6 +41,7 @@ SYMBOLS = {
                                  _P, _P, _I, _I, _P, _P, _P, _P]),
     "attn_prefill_varlen": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                  _I, _I, _I, _F, _I, _P, _I, _P, _P]),
+    "attn_smooth_quant_k": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "attn_gather_paged_kv": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -140,6 +142,14 @@ def attn_prefill_varlen(q, k, v_perm, qk_dtype, v_dtype, q_scale, k_scale, v_sca
                                      max_seqlen_k, total_q, total_k, num_q_heads, num_kv_heads,
                                      head_dim, float(sm_scale), int(causal), _ptr(o), o_dtype,
                                      _ptr(lse), s), "attn_prefill_varlen")
+
+
+def attn_smooth_quant_k(k, cu_seqlens, batch, max_seqlen, total_tokens, num_kv_heads, head_dim,
+                        block_tokens, codes, scales, mean, stream=None):
+    s = _stream(stream, k, codes)
+    _check(lib().attn_smooth_quant_k(_ptr(k), _ptr(cu_seqlens), batch, max_seqlen, total_tokens,
+                                     num_kv_heads, head_dim, block_tokens, _ptr(codes), _ptr(scales),
+                                     _ptr(mean), s), "attn_smooth_quant_k")
 
 
 def attn_gather_paged_kv(cache, elem_bytes, kv_indptr, kv_indices, kv_last_page_len, cu_seqlens_k,

@@ -9,6 +9,7 @@
 #include "../../include/attnq.h"
 #include "launch.h"
 #include "gather.h"
+#include "smooth.h"
 
 namespace {
 
@@ -245,6 +246,31 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
                    : qk_dtype == ATTNQ_BF16 ? attnq::PF_Q_RAW_BF16 : attnq::PF_Q_RAW_F16;
   LAUNCHED(attnq::launch_prefill(a, head_dim, q_mode, v_dtype == ATTNQ_FP8E4M3, o_dtype == ATTNQ_BF16,
                                  max_seqlen_q, stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------- attn_smooth_quant_k
+int attn_smooth_quant_k(const void* k, const int32_t* cu_seqlens, int batch, int max_seqlen,
+                        int total_tokens, int num_kv_heads, int head_dim, int block_tokens,
+                        void* codes, float* scales, float* mean, hipStream_t stream) {
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(block_tokens == 128, ATTNQ_EUNSUPPORTED, "block_tokens must be 128 (got %d)", block_tokens);
+  REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0 && num_kv_heads > 0, ATTNQ_EINVAL,
+          "batch, max_seqlen, total_tokens must be >= 0 and num_kv_heads > 0");
+  REQUIRE(num_kv_heads <= 65535, ATTNQ_EUNSUPPORTED, "num_kv_heads too large");
+  if (batch == 0) return ok();
+  REQUIRE_PTR(cu_seqlens, 4);
+  REQUIRE_PTR(mean, 4);
+  const int nblk = (max_seqlen + 127) / 128;
+  if (nblk > 0) {
+    REQUIRE_PTR(scales, 4);
+    if (total_tokens > 0) {
+      REQUIRE_PTR(k, 16);
+      REQUIRE_PTR(codes, 16);
+    }
+  }
+  LAUNCHED(attnq::launch_smooth_quant_int8_block(k, cu_seqlens, batch, num_kv_heads, head_dim, nblk,
+                                                 total_tokens, codes, scales, mean, stream));
   return ok();
 }
 

@@ -10,6 +10,7 @@
 // reciprocal per scale and a fused-multiply-add correction (quot_by_recip).
 #include "kcommon.h"
 #include "launch.h"
+#include "smooth.h"
 
 namespace attnq {
 
@@ -117,10 +118,13 @@ __global__ __launch_bounds__(FP8_THREADS) void k_quant_fp8(const uint16_t* __res
 constexpr int I8_THREADS = 256;
 constexpr int I8_BLOCK = 128;
 
-template <bool BF16, int DIM>
+// SMOOTH: the values quantized are x - mean[b][h][channel] (fp32, rounded
+// once), the sequence's per-channel mean of K written by k_channel_mean.
+template <bool BF16, int DIM, bool SMOOTH = false>
 __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int nblk,
-    int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales) {
+    int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales,
+    const float* __restrict__ mean = nullptr) {
   constexpr int CPR = DIM / 8;                          // 16-byte chunks per row
   constexpr int NCH = I8_BLOCK * CPR / I8_THREADS;      // chunks per thread
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -139,15 +143,25 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
     const int row = min(c / CPR, nrows - 1), col = (c % CPR) * 8;
     v[k] = *reinterpret_cast<const u32x4*>(x + ((long)(r0 + row) * heads + h) * DIM + col);
   }
+  // this thread's channels' means (the same 8 channels for every chunk of a row)
+  float mu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (SMOOTH) {
+    static_assert(I8_THREADS % CPR == 0, "a thread keeps its channel column");
+    const float* mp = mean + ((long)b * heads + h) * DIM + (threadIdx.x % CPR) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = mp[e];
+  }
+  auto val = [&](int k, int e) -> float {
+    const float xv = h16_to_f32(e & 1 ? v[k][e >> 1] >> 16 : v[k][e >> 1] & 0xffffu, BF16);
+    if constexpr (SMOOTH) return xv - mu[e];
+    else return xv;
+  };
   float m = 0.0f;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     if ((threadIdx.x + k * I8_THREADS) / CPR < nrows) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        m = fmaxf(m, fabsf(h16_to_f32(v[k][e] & 0xffffu, BF16)));
-        m = fmaxf(m, fabsf(h16_to_f32(v[k][e] >> 16, BF16)));
-      }
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(val(k, e)));
     }
   }
   __shared__ float s_red[I8_THREADS / 64];
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
         uint32_t q[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float xv = h16_to_f32(e & 1 ? v[k][e >> 1] >> 16 : v[k][e >> 1] & 0xffffu, BF16);
+          const float xv = val(k, e);
           q[e] = (uint32_t)int8_encode(FAST ? quot_by_recip_i8(xv, scale, rs) : xv / scale) & 0xffu;
         }
         *reinterpret_cast<u32x2*>(codes + ((long)(r0 + row) * heads + h) * DIM + col) =
@@ -180,6 +194,39 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
   };
   if (scale >= QUOT_MIN_SCALE) encode_all(std::true_type{});  // uniform
   else encode_all(std::false_type{});
+}
+
+// ---------------------------------------------------------------- per-channel mean of K
+// mean[b][h][c] of fp16 x over the tokens of sequence b: the exact sum S of
+// the values (each an integer number of 2^-24 units, accumulated in int64),
+// then fp32(fp64(S) / fp64(L)) * 2^-24; 0 for an empty sequence.  One
+// workgroup per (head, sequence); thread (row group g, channel c).
+constexpr int MEAN_THREADS = 256;
+
+template <int DIM>
+__global__ __launch_bounds__(MEAN_THREADS) void k_channel_mean(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int total_tokens,
+    float* __restrict__ mean) {
+  constexpr int G = MEAN_THREADS / DIM;  // row groups
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int c = threadIdx.x % DIM, g = threadIdx.x / DIM;
+  const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
+  long long acc = 0;
+  for (int t = s0 + g; t < s1; t += G) {
+    const double v = (double)f16_to_f32(x[((long)t * heads + h) * DIM + c]);
+    acc += (long long)(v * 16777216.0);  // exact: an integer below 2^40 in magnitude
+  }
+  __shared__ long long s_acc[MEAN_THREADS];
+  s_acc[threadIdx.x] = acc;
+  __syncthreads();
+  if (g == 0) {
+    long long tot = acc;
+#pragma unroll
+    for (int k = 1; k < G; ++k) tot += s_acc[k * DIM + c];
+    const int L = s1 - s0;
+    const float m = L > 0 ? (float)((double)tot / (double)L) * 5.9604644775390625e-08f : 0.0f;  // * 2^-24
+    mean[((long)b * heads + h) * DIM + c] = m;
+  }
 }
 
 // ---------------------------------------------------------------- V transpose / permute
@@ -321,6 +368,26 @@ bool launch_v_permute(const void* v, const int32_t* cu, int batch, int heads, in
                      static_cast<const uint16_t*>(v), cu, heads, dim, s_pad, (int)is_bf16,
                      total_tokens, (int)fp8, (int)wide, descale, out);
   return ok(hipGetLastError());
+}
+
+}  // namespace attnq
+
+namespace attnq {
+
+bool launch_smooth_quant_int8_block(const void* x, const int32_t* cu, int batch, int heads, int dim,
+                                    int nblk, int total_tokens, void* codes, float* scales, float* mean,
+                                    hipStream_t s) {
+  if (batch <= 0) return true;
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  int8_t* cp = static_cast<int8_t*>(codes);
+  if (dim == 128) hipLaunchKernelGGL((k_channel_mean<128>), dim3(heads, batch), dim3(MEAN_THREADS), 0, s, xp, cu, heads, total_tokens, mean);
+  else hipLaunchKernelGGL((k_channel_mean<64>), dim3(heads, batch), dim3(MEAN_THREADS), 0, s, xp, cu, heads, total_tokens, mean);
+  if (hipGetLastError() != hipSuccess) return false;
+  if (nblk <= 0) return true;
+  const dim3 grid(nblk, heads, batch);
+  if (dim == 128) hipLaunchKernelGGL((k_quant_int8_block<false, 128, true>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales, mean);
+  else hipLaunchKernelGGL((k_quant_int8_block<false, 64, true>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales, mean);
+  return hipGetLastError() == hipSuccess;
 }
 
 }  // namespace attnq

@@ -83,10 +83,13 @@ class SagePrefill:
     permuted transposed layout, int8 QK / fp16 PV prefill, fp16 output.
     With fuse_q (default) the prefill quantizes each 128-query block of the
     16-bit Q itself (same codes and scales as attn_quant_qk; the scales land
-    in qs) instead of reading int8 codes written by a separate pass."""
+    in qs) instead of reading int8 codes written by a separate pass.  With
+    smooth_k each sequence's per-channel mean of K (kept in kmean) is
+    subtracted before K's int8 quantization (attn_smooth_quant_k): the same
+    softmax output, with lse lower by sm_scale * q . mean."""
 
     def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False,
-                 fuse_q=True):
+                 fuse_q=True, smooth_k=False):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
@@ -95,6 +98,9 @@ class SagePrefill:
         self.max_seqlen = int(max_seqlen)
         self.sm_scale, self.causal = float(sm_scale), bool(causal)
         self.fuse_q = bool(fuse_q)
+        self.smooth_k = bool(smooth_k)
+        if self.smooth_k and k.dtype != torch.float16:
+            raise TypeError("K smoothing takes fp16 K")
         if v.dtype != torch.float16:
             raise TypeError("SagePrefill takes fp16 V (the PV product runs on fp16 V^T)")
         nblk = (self.max_seqlen + 127) // 128
@@ -102,6 +108,7 @@ class SagePrefill:
         self.kc = torch.empty(k.shape, dtype=torch.int8, device=dev)
         self.qs = torch.empty((self.b, self.hq, nblk), dtype=torch.float32, device=dev)
         self.ks = torch.empty((self.b, self.hkv, nblk), dtype=torch.float32, device=dev)
+        self.kmean = torch.empty((self.b, self.hkv, self.d), dtype=torch.float32, device=dev) if self.smooth_k else None
         self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_seqlen, 128)),
                               dtype=torch.float16, device=dev)
         self.o = torch.empty((self.t, self.hq, self.d), dtype=torch.float16, device=dev)
@@ -111,8 +118,12 @@ class SagePrefill:
         if not self.fuse_q:
             A.attn_quant_qk(self.q, _dtype_code(self.q), self.cu, self.b, self.max_seqlen, self.t,
                             self.hq, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs)
-        A.attn_quant_qk(self.k, _dtype_code(self.k), self.cu, self.b, self.max_seqlen, self.t,
-                        self.hkv, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
+        if self.smooth_k:
+            A.attn_smooth_quant_k(self.k, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d, 128,
+                                  self.kc, self.ks, self.kmean)
+        else:
+            A.attn_quant_qk(self.k, _dtype_code(self.k), self.cu, self.b, self.max_seqlen, self.t,
+                            self.hkv, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
         A.attn_quant_v_permute(self.v, A.FP16, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
                                self.d, A.Q_NONE, None, self.vp, None)
 

@@ -152,6 +152,22 @@ def test_gather_validation():
     assert _gather(mk=0, c=None) == 0
 
 
+def _smooth(**kw):
+    a = dict(k=FAKE, cu=FAKE, b=1, mx=10, t=10, h=2, d=128, bt=128, codes=FAKE, sc=FAKE, mean=FAKE, st=None)
+    a.update(kw)
+    return pk.lib().attn_smooth_quant_k(*a.values())
+
+
+def test_smooth_quant_k_validation():
+    assert _smooth(d=96) == -2 and "head_dim" in _err()
+    assert _smooth(bt=64) == -2 and "block_tokens" in _err()
+    assert _smooth(h=0) == -1
+    assert _smooth(t=-1) == -1
+    assert _smooth(mean=None) == -1 and "mean" in _err()
+    assert _smooth(codes=FAKE + 4) == -1 and "aligned" in _err()
+    assert _smooth(b=0, k=None, cu=None, mean=None) == 0     # nothing to do: no pointer is needed
+
+
 def _mla(**kw):
     a = dict(q=FAKE, c=FAKE, bt=FAKE, mb=4, kl=FAKE, idx=FAKE, topk=8, b=1, sq=1, h=16, nb=8, bs=64,
              sc=0.04, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, st=None)

@@ -329,3 +329,29 @@ def test_ragged_from_pages_returns_what_the_append_wrote():
     last = (lens - (npg - 1) * 4).astype(np.int32)
     assert np.array_equal(ragged_from_pages(kc2, x["kv_indptr"], x["kv_indices"], last, x["cu_seqlens"]), k_rot)
     assert np.array_equal(ragged_from_pages(vc2, x["kv_indptr"], x["kv_indices"], last, x["cu_seqlens"]), x["v"])
+
+
+def test_k_smoothing_leaves_softmax_output_unchanged():
+    """Subtracting a per-sequence, per-channel mean from K moves every logit
+    of a query by the same amount: O is unchanged, lse moves by sm * q . mean."""
+    rng = np.random.default_rng(40)
+    lens_q, lens_k = [5, 3], [9, 3]
+    cu_q = np.array([0, 5, 8], np.int32)
+    cu_k = np.array([0, 9, 12], np.int32)
+    q = rng.standard_normal((8, 4, 16))
+    k = rng.standard_normal((12, 2, 16)) + rng.standard_normal((1, 2, 16)) * 3
+    v = rng.standard_normal((12, 2, 16))
+    ks = k.copy()
+    means = []
+    for b in range(2):
+        m = k[cu_k[b]:cu_k[b + 1]].mean(axis=0)
+        ks[cu_k[b]:cu_k[b + 1]] -= m
+        means.append(m)
+    a = prefill_varlen(q, k, v, cu_q, cu_k, 0.3, True, "bf16")
+    s = prefill_varlen(q, ks, v, cu_q, cu_k, 0.3, True, "bf16")
+    assert np.abs(a["o_exact"] - s["o_exact"]).max() < 1e-12
+    for b in range(2):
+        for i in range(cu_q[b], cu_q[b + 1]):
+            for h in range(4):
+                shift = 0.3 * float(q[i, h] @ means[b][h // 2])
+                assert abs(float(a["lse"][h, i]) - float(s["lse"][h, i]) - shift) < 1e-4

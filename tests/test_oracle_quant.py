@@ -104,3 +104,56 @@ def test_v_permute_inverse_and_padding(fp8):
     for b, L in enumerate(lens):
         pad = np.setdiff1d(np.arange(128), pos_of[:L])
         assert not out[b][:, :, pad].any()
+
+
+# ---------------------------------------------------------------------------
+# K smoothing (per-sequence, per-channel mean subtracted before int8 quant)
+# ---------------------------------------------------------------------------
+def _sage_small(seed=31, lens=(300, 1, 0, 129)):
+    return gen.sage_inputs(seed, list(lens), 4, 2, 64)
+
+
+def test_channel_mean_vs_exact_rationals():
+    from fractions import Fraction
+    from oracle.quant import channel_mean_fp16
+    x = _sage_small()
+    k, cu = x["k"], x["cu_seqlens"]
+    m = channel_mean_fp16(k, cu)
+    rng = np.random.default_rng(0)
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        for h, c in zip(rng.integers(0, 2, 6), rng.integers(0, 64, 6)):
+            if s1 == s0:
+                assert m[b, h, c] == 0.0
+                continue
+            exact = sum(Fraction(float(v)) for v in k[s0:s1, h, c].astype(np.float64)) / (s1 - s0)
+            got = Fraction(float(m[b, h, c]))
+            # two roundings after an exact sum: within one fp32 ulp of the exact mean
+            ulp = Fraction(float(np.spacing(np.float32(abs(float(exact)) or 1e-30))))
+            assert abs(got - exact) <= ulp
+
+
+def test_channel_mean_independent_of_token_order_and_exact_on_constants():
+    from oracle.quant import channel_mean_fp16
+    x = _sage_small(32, (257,))
+    k, cu = x["k"], x["cu_seqlens"]
+    perm = np.random.default_rng(1).permutation(257)
+    assert np.array_equal(channel_mean_fp16(k, cu).view(np.uint32), channel_mean_fp16(k[perm], cu).view(np.uint32))
+    const = np.full((5, 1, 64), np.float16(-3.140625), np.float16)
+    assert np.all(channel_mean_fp16(const, np.array([0, 5], np.int32)) == np.float32(-3.140625))
+
+
+def test_smoothing_shrinks_int8_error_with_channel_offsets():
+    from oracle.quant import smooth_quant_k
+    from oracle.attention import dequant_int8_per_block
+    x = gen.sage_inputs(33, [700, 400], 4, 2, 128, offset_frac=0.05, offset_sd=4.0)
+    k, cu = x["k"], x["cu_seqlens"]
+    k32 = as_f32(k, "fp16").astype(np.float64)
+    c0, s0 = quant_int8_per_block(k, "fp16", cu, 700)
+    c1, s1, mean = smooth_quant_k(k, cu, 700)
+    e0 = np.abs(dequant_int8_per_block(c0, s0, cu) - k32).mean()
+    back = dequant_int8_per_block(c1, s1, cu)
+    for b in range(2):
+        back[cu[b]:cu[b + 1]] += mean[b][None].astype(np.float64)
+    e1 = np.abs(back - k32).mean()
+    assert e1 < 0.8 * e0, (e0, e1)
