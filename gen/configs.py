@@ -209,10 +209,13 @@ def config5() -> dict:
 # SageAttention-style INT8 prefill (config 2)
 # ---------------------------------------------------------------------------
 def sage_inputs(seed: int, seqlens, hq: int, hkv: int, d: int,
-                offset_frac: float = 0.01, offset_sd: float = 2.0) -> dict:
+                offset_frac: float = 0.01, offset_sd: float = 2.0,
+                v_channel_sd: float = 0.0) -> dict:
     """fp16 Q/K/V, N(0,1); in Q and in K (independently) round(frac*H*d)
     distinct (head, channel) pairs get one N(0, offset_sd^2) offset added to
-    every token."""
+    every token.  v_channel_sd > 0: every (head, channel) of V is multiplied
+    by exp(N(0, v_channel_sd^2)) (channels of unequal magnitude; drawn after
+    everything else, so the other tensors do not change)."""
     rng = np.random.default_rng(seed)
     cu = _cu(seqlens)
     t = int(cu[-1])
@@ -226,7 +229,10 @@ def sage_inputs(seed: int, seqlens, hq: int, hkv: int, d: int,
         x.reshape(t, h * d)[:, pairs] += offs[None, :]
         out[name] = x.astype(np.float16)
         out[name + "_offset_channels"] = pairs.astype(np.int32)
-    out["v"] = _normal_f32(rng, (t, hkv, d)).astype(np.float16)
+    v = _normal_f32(rng, (t, hkv, d))
+    if v_channel_sd > 0:
+        v *= np.exp(rng.normal(0.0, v_channel_sd, size=(1, hkv, d))).astype(np.float32)
+    out["v"] = v.astype(np.float16)
     return out
 
 

@@ -56,6 +56,16 @@ def dequant_fp8_per_head(codes: np.ndarray, descale: np.ndarray) -> np.ndarray:
     return e4m3fn_decode(codes) * np.asarray(descale, np.float64)[None, :, None]
 
 
+def dequant_fp8_per_channel(codes: np.ndarray, descale: np.ndarray, cu_seqlens) -> np.ndarray:
+    """codes [T, H, D] uint8, descale [B, H, D] -> fp64 values code * descale
+    of the token's sequence."""
+    out = np.zeros(codes.shape, np.float64)
+    for b in range(len(cu_seqlens) - 1):
+        s0, s1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        out[s0:s1] = e4m3fn_decode(codes[s0:s1]) * np.asarray(descale[b], np.float64)[None, :, :]
+    return out
+
+
 def dequant_int8_per_block(codes: np.ndarray, scales: np.ndarray, cu_seqlens,
                            block_tokens: int = 128) -> np.ndarray:
     """codes [T, H, D] int8, scales [B, H, nblk] -> fp64 values."""

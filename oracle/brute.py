@@ -74,6 +74,26 @@ def quant_fp8_per_head(x32: np.ndarray):
     return codes, ds
 
 
+def quant_fp8_per_channel(x32: np.ndarray, cu):
+    """x32 [T, H, D] fp32 -> (codes [T,H,D], descale [B,H,D]) by scalar loops:
+    one descale per (sequence, head, channel)."""
+    t, h, d = x32.shape
+    b = len(cu) - 1
+    codes = np.zeros((t, h, d), np.uint8)
+    ds = np.ones((b, h, d), np.float32)
+    for bi in range(b):
+        for hh in range(h):
+            for k in range(d):
+                amax = 0.0
+                for i in range(int(cu[bi]), int(cu[bi + 1])):
+                    amax = max(amax, abs(float(x32[i, hh, k])))
+                desc = f32(1.0) if amax == 0 else f32(amax) / f32(448.0)
+                ds[bi, hh, k] = desc
+                for i in range(int(cu[bi]), int(cu[bi + 1])):
+                    codes[i, hh, k] = e4m3fn_encode_search(float(f32(x32[i, hh, k]) / desc))
+    return codes, ds
+
+
 def quant_int8_per_block(x32: np.ndarray, cu, block: int):
     t, h, d = x32.shape
     codes = np.zeros((t, h, d), np.int8)

@@ -21,13 +21,19 @@ Token permutation pi inside a 32-token group (j in [0, 32)):
     half = j // 16, g = (j % 16) // 4, r = j % 4  ->  pi(j) = 8 g + 4 half + r
 so stored position p = 8 g + s holds token (s // 4) * 16 + 4 g + s % 4.
 
+* ``quant_fp8_per_channel`` -- SageAttention's fp8 V with one descale per
+  channel.  The pages give fp8 V only with per-head descales; reading: one
+  descale per (sequence, kv head, channel), amax over the sequence's tokens,
+  descale = amax / 448 (IEEE fp32), 1 where amax = 0 (so also for an empty
+  sequence); codes as in ``quant_fp8_per_head``.  ``v_permute`` takes the
+  same option.
 * ``channel_mean_fp16`` / ``smooth_quant_k`` -- SageAttention's K smoothing
   before the int8 block quantization: subtract each sequence's per-channel
   mean of K (softmax-invariant).  Reading: exact sum, mean = fp32(fp64(S)/L),
   then codes of fp32(k) - mean.
 
 Pins (tests/test_oracle_quant.py): amax and descale by exhaustive
-comparison with a per-element Python max; codes against the brute-force
+comparison with a per-element Python max (per head and per channel); codes against the brute-force
 nearest-grid encoder; block boundaries at sequence starts; pi is a
 bijection and its inverse recovers V bit-exactly; padding is +0; the
 channel mean against exact rational arithmetic, its independence of token
@@ -87,6 +93,24 @@ def quant_fp8_per_head(x: np.ndarray, dtype: str, amax_in=None):
     return e4m3fn_encode(v), ds
 
 
+def quant_fp8_per_channel(x: np.ndarray, dtype: str, cu_seqlens):
+    """x [T, H, D] -> (codes uint8 [T,H,D], descale f32 [B, H, D]): the
+    descale of (b, h, c) is fp8_descale of max |x| over sequence b's tokens
+    in channel c of head h."""
+    x32 = as_f32(x, dtype)
+    t, h, d = x32.shape
+    cu = np.asarray(cu_seqlens, np.int64)
+    b = len(cu) - 1
+    codes = np.zeros((t, h, d), np.uint8)
+    ds = np.ones((b, h, d), np.float32)
+    for bi in range(b):
+        s0, s1 = int(cu[bi]), int(cu[bi + 1])
+        if s1 > s0:
+            ds[bi] = fp8_descale(np.abs(x32[s0:s1]).max(axis=0))
+            codes[s0:s1] = e4m3fn_encode(x32[s0:s1] / ds[bi][None, :, :])
+    return codes, ds
+
+
 def quant_int8_per_block(x: np.ndarray, dtype: str, cu_seqlens: np.ndarray,
                          max_seqlen: int, block_tokens: int = 128):
     """x [T, H, D] -> (codes int8 [T,H,D], scales f32 [B, H, ceil(max_seqlen/block)]).
@@ -124,18 +148,22 @@ def s_pad(max_seqlen: int) -> int:
 
 
 def v_permute(v: np.ndarray, dtype: str, cu_seqlens: np.ndarray, max_seqlen: int,
-              fp8: bool, amax_in=None):
-    """V [T, H, D] -> (v_out [B, H, D, S_pad], descale f32[H] or None).
+              fp8: bool, amax_in=None, per_channel: bool = False):
+    """V [T, H, D] -> (v_out [B, H, D, S_pad], descale f32[H], [B, H, D] or None).
 
     v_out[b, h, d, 32*G + pi(j)] = enc(V[cu[b] + 32*G + j, h, d]) for tokens
     32*G + j < L_b, and the all-zero pattern (+0) past L_b.  enc is the
-    e4m3fn code with the per-head descale (fp8=True) or the unchanged 16-bit
-    pattern (fp8=False)."""
+    e4m3fn code with the per-head descale (fp8=True), with the per-channel
+    descale (fp8=True, per_channel=True), or the unchanged 16-bit pattern
+    (fp8=False)."""
     t, h, d = v.shape
     b = len(cu_seqlens) - 1
     sp = s_pad(max_seqlen)
     if fp8:
-        codes, ds = quant_fp8_per_head(v, dtype, amax_in)
+        if per_channel:
+            codes, ds = quant_fp8_per_channel(v, dtype, cu_seqlens)
+        else:
+            codes, ds = quant_fp8_per_head(v, dtype, amax_in)
         src = codes
         out = np.zeros((b, h, d, sp), np.uint8)
     else:

@@ -4,8 +4,8 @@ import pytest
 
 import gen
 from oracle import brute
-from oracle.quant import (as_f32, quant_fp8_per_head, quant_int8_per_block, v_permute,
-                          v_unpermute, perm_pi, s_pad, fp8_descale)
+from oracle.quant import (as_f32, quant_fp8_per_head, quant_fp8_per_channel, quant_int8_per_block,
+                          v_permute, v_unpermute, perm_pi, s_pad, fp8_descale)
 from oracle.numerics import e4m3fn_decode
 
 
@@ -42,6 +42,59 @@ def test_fp8_descale_is_amax_over_448_and_zero_head():
     c2, d2 = quant_fp8_per_head(x, "bf16", amax_in=a.max(axis=(0, 2)))
     assert np.array_equal(c2, codes) and np.array_equal(d2, ds)
     assert fp8_descale(np.array([0.0, 448.0]))[1] == 1.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fp8_per_channel_vs_brute(dtype):
+    x, cu = _tiny(5, [3, 5, 0, 1], 2, 4, dtype)
+    codes, ds = quant_fp8_per_channel(x, dtype, cu)
+    bc, bds = brute.quant_fp8_per_channel(as_f32(x, dtype), cu)
+    assert ds.shape == (4, 2, 4)
+    assert np.array_equal(ds.view(np.uint32), bds.view(np.uint32))
+    assert np.array_equal(codes, bc)
+    assert (ds[2] == 1.0).all()                  # the empty sequence
+    from oracle.attention import dequant_fp8_per_channel
+    deq = dequant_fp8_per_channel(codes, ds, cu)
+    seq_of = np.repeat(np.arange(4), np.diff(cu))
+    for i, h, c in np.ndindex(*codes.shape):
+        assert deq[i, h, c] == brute.e4m3fn_value(int(bc[i, h, c])) * float(bds[seq_of[i], h, c])
+
+
+def test_fp8_per_channel_reduces_to_per_head_when_channel_maxima_agree():
+    # one sequence whose channels of a head share one amax (token 0 holds
+    # +-A in every channel): each channel descale is the head's, and so are the codes
+    x, cu = _tiny(6, [40], 3, 8, "fp16")
+    x32 = as_f32(x, "fp16")
+    amax = np.abs(x32).max(axis=(0, 2)) * 2
+    signs = np.where(np.arange(8) % 2 == 0, 1.0, -1.0)
+    x = x32.copy()
+    x[0] = amax[:, None] * signs[None, :]
+    x = x.astype(np.float16)
+    c1, d1 = quant_fp8_per_channel(x, "fp16", cu)
+    c0, d0 = quant_fp8_per_head(x, "fp16")
+    assert np.array_equal(d1[0], np.repeat(d0[:, None], 8, axis=1))
+    assert np.array_equal(c1, c0)
+
+
+def test_fp8_per_channel_keeps_a_small_channel_that_per_head_flushes():
+    # head 0: channel 0 ~ 1000 N(0,1), channel 1 ~ 0.004 N(0,1).  With the
+    # head's descale (about amax/448 = 8) channel 1 lands below half of
+    # e4m3's smallest subnormal 2^-9 and mostly encodes to 0; with its own
+    # descale every value is a normal e4m3 number (relative error <= 2^-4)
+    # or a subnormal well below the channel's magnitude
+    from oracle.attention import dequant_fp8_per_head, dequant_fp8_per_channel
+    rng = np.random.default_rng(7)
+    x = np.zeros((256, 1, 2), np.float32)
+    x[:, 0, 0] = rng.standard_normal(256) * 1000
+    x[:, 0, 1] = rng.standard_normal(256) * 0.004
+    x = x.astype(np.float16)
+    cu = np.array([0, 256], np.int32)
+    v = as_f32(x, "fp16").astype(np.float64)[:, 0, 1]
+    ph = dequant_fp8_per_head(*quant_fp8_per_head(x, "fp16"))[:, 0, 1]
+    pc = dequant_fp8_per_channel(*quant_fp8_per_channel(x, "fp16", cu), cu)[:, 0, 1]
+    assert (ph == 0).mean() > 0.5
+    assert np.abs(ph - v).mean() > 0.5 * np.abs(v).mean()
+    assert np.abs(pc - v).mean() < 2.0 ** -4 * np.abs(v).mean()
 
 
 def test_int8_per_block_vs_brute():
@@ -86,14 +139,18 @@ def test_pi_definition_and_bijection():
     assert p[0] == 0 and p[17] == 5 and p[4] == 8 and p[31] == 31 and p[16] == 4
 
 
-@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fp8", [False, True, "per_channel"])
 def test_v_permute_inverse_and_padding(fp8):
     lens = [37, 64, 1]
     x, cu = _tiny(4, lens, 2, 8, "bf16")
-    out, ds = v_permute(x, "bf16", cu, max(lens), fp8=fp8)
+    out, ds = v_permute(x, "bf16", cu, max(lens), fp8=bool(fp8), per_channel=fp8 == "per_channel")
     assert out.shape == (3, 2, 8, s_pad(64)) and s_pad(64) == 128
     rec = v_unpermute(out, lens)
-    ref = quant_fp8_per_head(x, "bf16")[0] if fp8 else x
+    if fp8 == "per_channel":
+        ref, d1 = quant_fp8_per_channel(x, "bf16", cu)
+        assert np.array_equal(ds, d1) and ds.shape == (3, 2, 8)
+    else:
+        ref = quant_fp8_per_head(x, "bf16")[0] if fp8 else x
     for b in range(3):
         assert np.array_equal(rec[b], ref[cu[b]:cu[b + 1]])
     # explicit placement: token 17 of sequence 0, head 1, channel 3
