@@ -214,8 +214,9 @@ def sage_inputs(seed: int, seqlens, hq: int, hkv: int, d: int,
     """fp16 Q/K/V, N(0,1); in Q and in K (independently) round(frac*H*d)
     distinct (head, channel) pairs get one N(0, offset_sd^2) offset added to
     every token.  v_channel_sd > 0: every (head, channel) of V is multiplied
-    by exp(N(0, v_channel_sd^2)) (channels of unequal magnitude; drawn after
-    everything else, so the other tensors do not change)."""
+    by f = exp(N(0, v_channel_sd^2)) / (the largest f of its head), so the
+    largest channel of a head stays N(0,1) and the others are smaller
+    (drawn after everything else, so the other tensors do not change)."""
     rng = np.random.default_rng(seed)
     cu = _cu(seqlens)
     t = int(cu[-1])
@@ -231,7 +232,8 @@ def sage_inputs(seed: int, seqlens, hq: int, hkv: int, d: int,
         out[name + "_offset_channels"] = pairs.astype(np.int32)
     v = _normal_f32(rng, (t, hkv, d))
     if v_channel_sd > 0:
-        v *= np.exp(rng.normal(0.0, v_channel_sd, size=(1, hkv, d))).astype(np.float32)
+        f = np.exp(rng.normal(0.0, v_channel_sd, size=(1, hkv, d)))
+        v *= (f / f.max(axis=2, keepdims=True)).astype(np.float32)
     out["v"] = v.astype(np.float16)
     return out
 

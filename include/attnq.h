@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTNQ_ABI_VERSION 1
+#define ATTNQ_ABI_VERSION 2
 
 typedef enum {
   ATTNQ_OK = 0,
@@ -55,8 +55,12 @@ typedef enum {
   ATTNQ_Q_INT8_PER_BLOCK = 1, /* int8 codes, one fp32 scale per (seq, head, 128-token block) */
   ATTNQ_Q_NONE = 2,           /* unquantized 16-bit data */
   ATTNQ_Q_FP8_PER_HEAD_WIDE = 3, /* fp8 e4m3fn codes as above, each stored as its exact fp16 value */
-  ATTNQ_Q_INT8_PER_BLOCK_RAW_Q = 4 /* attn_prefill_varlen only: 16-bit Q quantized inside the call as
-                                      INT8_PER_BLOCK, int8 per-block K */
+  ATTNQ_Q_INT8_PER_BLOCK_RAW_Q = 4, /* attn_prefill_varlen only: 16-bit Q quantized inside the call as
+                                       INT8_PER_BLOCK, int8 per-block K */
+  ATTNQ_Q_FP8_PER_CHANNEL = 5,      /* V only: e4m3fn codes, one fp32 descale per (sequence, kv head,
+                                       channel) */
+  ATTNQ_Q_FP8_PER_CHANNEL_WIDE = 6  /* V only: the codes of FP8_PER_CHANNEL stored as their exact
+                                       fp16 values */
 } attnq_qmode;
 
 int attnq_abi_version(void);
@@ -101,6 +105,12 @@ int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int bat
  *          its value in fp16 (exact for every finite e4m3fn code), 2 bytes/element:
  *          the prefill then stages V with no widening step (pass v_dtype FP16
  *          and the descales as v_scale);
+ *          FP8_PER_CHANNEL / FP8_PER_CHANNEL_WIDE (SageAttention's fp8 V with a
+ *          scale per channel; the pages give V descales per head only): as the
+ *          two modes above, but v_scales is fp32 [batch, num_kv_heads, head_dim]
+ *          (16-byte aligned for the prefill) and receives descale = amax/448
+ *          with amax over the sequence's tokens in that channel (1 if amax = 0,
+ *          so also for an empty sequence); amax_in must be NULL;
  *          NONE: enc = the unchanged 16-bit value, v_scales ignored.
  *   amax_in optional, as in attn_quant_qk.
  */
@@ -153,8 +163,12 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  *     [B, Hq, ceil(max_seqlen_q/128)] receiving the scale of every block that holds
  *     a query (other entries are left as they are).  The codes never reach memory.
  *   v_perm: attn_quant_v_permute's output for the keys, [B, Hkv, D, round_up(max_seqlen_k,128)];
- *     v_dtype FP8E4M3 (v_scale [Hkv] required) or FP16 (v_scale optional: when
- *     given, V = value * v_scale[kv head], as for FP8_PER_HEAD_WIDE).  The padding
+ *     v_dtype FP8E4M3 (v_scale required) or FP16 (v_scale optional: when given,
+ *     V = value * descale, as for the _WIDE modes).  v_scale_mode FP8_PER_HEAD:
+ *     v_scale [Hkv], one descale per kv head; FP8_PER_CHANNEL: v_scale [B, Hkv, D]
+ *     as written by attn_quant_v_permute's per-channel modes (required, 16-byte
+ *     aligned), V[j][d] = value * v_scale[b][kv head][d], applied to the output
+ *     column d after the PV product.  The padding
  *     past each sequence's keys must hold finite values (attn_quant_v_permute
  *     writes zeros there): it meets p = 0 in the PV product.
  *   logit(i, j) = sm_scale * Dequant(q_i) . Dequant(k_j); q head h reads kv head
@@ -169,7 +183,7 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  */
 int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk_dtype,
                         int v_dtype, const float* q_scale, const float* k_scale,
-                        const float* v_scale, int scale_mode, const int32_t* cu_seqlens_q,
+                        const float* v_scale, int v_scale_mode, int scale_mode, const int32_t* cu_seqlens_q,
                         const int32_t* cu_seqlens_k, int batch, int max_seqlen_q,
                         int max_seqlen_k, int total_q, int total_k, int num_q_heads,
                         int num_kv_heads, int head_dim, float sm_scale, int causal, void* o,

@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "BF16", "FP16", "FP8E4M3", "INT8", "Q_FP8_PER_HEAD", "Q_INT8_PER_BLOCK", "Q_NONE", "Q_FP8_PER_HEAD_WIDE",
+    "BF16", "FP16", "FP8E4M3", "INT8", "Q_FP8_PER_HEAD", "Q_INT8_PER_BLOCK", "Q_NONE", "Q_FP8_PER_HEAD_WIDE", "Q_FP8_PER_CHANNEL", "Q_FP8_PER_CHANNEL_WIDE",
     "Q_INT8_PER_BLOCK_RAW_Q",
     "library_path", "lib", "abi_version",
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
@@ -25,6 +25,7 @@ __all__ = [
 
 BF16, FP16, FP8E4M3, INT8 = 0, 1, 2, 3
 Q_FP8_PER_HEAD, Q_INT8_PER_BLOCK, Q_NONE, Q_FP8_PER_HEAD_WIDE, Q_INT8_PER_BLOCK_RAW_Q = 0, 1, 2, 3, 4
+Q_FP8_PER_CHANNEL, Q_FP8_PER_CHANNEL_WIDE = 5, 6
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -39,8 +40,8 @@ SYMBOLS = {
     "attn_quant_v_permute": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "attn_append_kv_rope": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P,
                                  _P, _P, _I, _I, _P, _P, _P, _P]),
-    "attn_prefill_varlen": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
-                                 _I, _I, _I, _F, _I, _P, _I, _P, _P]),
+    "attn_prefill_varlen": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I,
+                                 _I, _I, _I, _I, _F, _I, _P, _I, _P, _P]),
     "attn_smooth_quant_k": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "attn_gather_paged_kv": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
@@ -131,13 +132,13 @@ def attn_append_kv_rope(q, k, v, dtype, cu_seqlens, kv_len_before, batch, total_
                                      _ptr(amax_k), _ptr(amax_v), s), "attn_append_kv_rope")
 
 
-def attn_prefill_varlen(q, k, v_perm, qk_dtype, v_dtype, q_scale, k_scale, v_scale, scale_mode,
+def attn_prefill_varlen(q, k, v_perm, qk_dtype, v_dtype, q_scale, k_scale, v_scale, v_scale_mode, scale_mode,
                         cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, total_q,
                         total_k, num_q_heads, num_kv_heads, head_dim, sm_scale, causal, o,
                         o_dtype, lse=None, stream=None):
     s = _stream(stream, q, o)
     _check(lib().attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v_perm), qk_dtype, v_dtype,
-                                     _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), scale_mode,
+                                     _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), v_scale_mode, scale_mode,
                                      _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, max_seqlen_q,
                                      max_seqlen_k, total_q, total_k, num_q_heads, num_kv_heads,
                                      head_dim, float(sm_scale), int(causal), _ptr(o), o_dtype,

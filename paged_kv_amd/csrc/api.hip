@@ -114,14 +114,26 @@ int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, 
   REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   REQUIRE(num_kv_heads > 0 && num_kv_heads <= 1024, ATTNQ_EINVAL, "num_kv_heads must be in [1, 1024]");
   REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0, ATTNQ_EINVAL, "sizes must be >= 0");
-  REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_FP8_PER_HEAD_WIDE || mode == ATTNQ_Q_NONE, ATTNQ_EINVAL,
-          "mode must be FP8_PER_HEAD, FP8_PER_HEAD_WIDE or NONE");
+  const bool chan = mode == ATTNQ_Q_FP8_PER_CHANNEL || mode == ATTNQ_Q_FP8_PER_CHANNEL_WIDE;
+  REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_FP8_PER_HEAD_WIDE || mode == ATTNQ_Q_NONE || chan,
+          ATTNQ_EINVAL, "mode must be FP8_PER_HEAD, FP8_PER_HEAD_WIDE, FP8_PER_CHANNEL, FP8_PER_CHANNEL_WIDE or NONE");
+  REQUIRE(!chan || !amax_in, ATTNQ_EINVAL, "amax_in holds per-head maxima: not accepted with a per-channel mode");
+  REQUIRE(!chan || (long)batch * num_kv_heads * head_dim < (1L << 31), ATTNQ_EUNSUPPORTED,
+          "batch * num_kv_heads * head_dim must stay below 2^31");
   REQUIRE_PTR(cu_seqlens, 4);
   REQUIRE_OPT_PTR(amax_in, 4);
   const int s_pad = round_up(max_seqlen, 128);
   if (batch > 0 && s_pad > 0) REQUIRE_PTR(v_out, 16);
   if (total_tokens > 0) REQUIRE_PTR(v, 16);
   const bool bf = v_dtype == ATTNQ_BF16;
+  if (chan) {
+    if (batch == 0) return ok();
+    REQUIRE_PTR(v_scales, 4);
+    LAUNCHED(attnq::launch_v_permute_per_channel(v, cu_seqlens, batch, num_kv_heads, head_dim, s_pad, bf,
+                                                 total_tokens, mode == ATTNQ_Q_FP8_PER_CHANNEL_WIDE,
+                                                 v_scales, v_out, stream));
+    return ok();
+  }
   const bool wide = mode == ATTNQ_Q_FP8_PER_HEAD_WIDE;
   const bool fp8 = mode == ATTNQ_Q_FP8_PER_HEAD || wide;
   if (fp8) {
@@ -182,7 +194,7 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
 // ---------------------------------------------------------------- attn_prefill_varlen
 int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk_dtype,
                         int v_dtype, const float* q_scale, const float* k_scale,
-                        const float* v_scale, int scale_mode, const int32_t* cu_seqlens_q,
+                        const float* v_scale, int v_scale_mode, int scale_mode, const int32_t* cu_seqlens_q,
                         const int32_t* cu_seqlens_k, int batch, int max_seqlen_q,
                         int max_seqlen_k, int total_q, int total_k, int num_q_heads,
                         int num_kv_heads, int head_dim, float sm_scale, int causal, void* o,
@@ -214,7 +226,11 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   if (rawq) REQUIRE_OPT_PTR(q_scale, 4);  // an output in this mode
   else REQUIRE_PTR(q_scale, 4);
   REQUIRE_PTR(k_scale, 4);
-  if (v_dtype == ATTNQ_FP8E4M3) REQUIRE_PTR(v_scale, 4);
+  REQUIRE(v_scale_mode == ATTNQ_Q_FP8_PER_HEAD || v_scale_mode == ATTNQ_Q_FP8_PER_CHANNEL, ATTNQ_EINVAL,
+          "v_scale_mode must be FP8_PER_HEAD or FP8_PER_CHANNEL");
+  const bool v_chan = v_scale_mode == ATTNQ_Q_FP8_PER_CHANNEL;
+  if (v_chan) REQUIRE_PTR(v_scale, 16);  // read as 4-float vectors
+  else if (v_dtype == ATTNQ_FP8E4M3) REQUIRE_PTR(v_scale, 4);
   else REQUIRE_OPT_PTR(v_scale, 4);
   if (total_q > 0) {
     REQUIRE_PTR(q, 16);
@@ -228,6 +244,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   attnq::PrefillArgs a;
   a.q = q; a.k = k; a.v = v_perm;
   a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.v_chan = v_chan ? 1 : 0;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
   a.o = o; a.lse = lse;
   a.q_scale_out = rawq ? const_cast<float*>(q_scale) : nullptr;

@@ -34,7 +34,7 @@ struct PrefillArgs {
   const void* v;          // permuted V^T [B, Hkv, D, s_pad]
   const float* q_scale;
   const float* k_scale;
-  const float* v_scale;
+  const float* v_scale;   // [Hkv], or [B, Hkv, D] when v_chan
   const int32_t* cu_q;
   const int32_t* cu_k;
   void* o;
@@ -42,6 +42,7 @@ struct PrefillArgs {
   float* q_scale_out;     // 16-bit Q quantized in the kernel: block scales written here (nullable)
   int batch, hq, hkv, s_pad, nblk_q, nblk_k, total_q, total_k, causal, max_q, max_k;
   int tblk;               // query tiles per block of the workgroup order (set by launch_prefill)
+  int v_chan;             // v_scale holds one descale per (sequence, kv head, channel)
   float sm_scale_log2;    // sm_scale * log2(e)
 };
 // Q/K forms of the prefill: fp8 codes with per-head descales; int8 codes with

@@ -51,8 +51,6 @@ constexpr int PF_BN = 64;   // keys per tile
 constexpr int PF_NST = 3;   // LDS stages of the DMA ring (two tiles in flight)
 constexpr int PF_TBLK_WGS = 64;  // workgroups per K/V stream in one block of the work order
 constexpr float PF_LN2 = 0.69314718055994530942f;
-constexpr float PF_I8_BIAS_F = 12582912.0f;  // 1.5 * 2^23
-constexpr int PF_I8_BIAS_BITS = 0x4B400000;  // its bits
 // buffer descriptor word 3 for untyped 32-bit accesses
 constexpr int PF_RSRC_W3 = 0x00020000;
 
@@ -426,20 +424,21 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if constexpr (QK_I8) {
-          // The accumulator starts at the bits of 1.5 * 2^23, so its integer
-          // sum s (|s| < 2^21) comes out as the bits of the float
-          // 1.5 * 2^23 + s, exactly: no int-to-float conversion per score.
-          // (Each element passes an empty asm before the bit cast: bit-casting
-          // elements of an int MFMA result straight to float makes this
-          // compiler read element 0 for all four.)
-          v4i acc = v4i{PF_I8_BIAS_BITS, PF_I8_BIAS_BITS, PF_I8_BIAS_BITS, PF_I8_BIAS_BITS};
+          // The integer sum (|s| < 2^21) converts to float exactly.  (A
+          // float bias in the accumulator would save this conversion, but the
+          // bias times the tile's scale is then rounded inside the exp2
+          // argument: an error of up to ~1.5 * fold in every logit of a tile.)
+          // Each element passes an empty asm first: reading elements of an
+          // int MFMA result one by one otherwise makes this compiler read
+          // element 0 for all four.
+          v4i acc = v4i{0, 0, 0, 0};
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qop[qb][0], acc, 0, 0, 0);
           if constexpr (QB == 32) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb2, qop[qb][1], acc, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             int bits = acc[r];
             asm("" : "+v"(bits));
-            s[kb][qb][r] = __builtin_bit_cast(float, bits);
+            s[kb][qb][r] = (float)bits;
           }
         } else {
           const v8i kop = v8i{ka[0], ka[1], ka[2], ka[3], kb2[0], kb2[1], kb2[2], kb2[3]};
@@ -466,8 +465,6 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
       fold = base_fold * k_sc_blk[kt >> 1];
     else
       fold = base_fold * k_sc_head;
-    // the scores' bias (int8: s carries 1.5 * 2^23) in log2 units
-    const float boff = QK_I8 ? PF_I8_BIAS_F * fold : 0.0f;
 
     // ---- mask (only tiles that cross the causal diagonal or the sequence end)
     const bool need_mask = kfirst + PF_BN > min(Lk, wq0 + off + 1);
@@ -492,7 +489,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     float lt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float neg_m = -m_ref[qb] - boff;
+      const float neg_m = -m_ref[qb];
       lt[qb] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -518,14 +515,13 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
           for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][qb][r]);
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
-        if constexpr (QK_I8) m -= PF_I8_BIAS_F;           // exact (or -inf)
         const float m_new = fmaxf(m_ref[qb], m * fold);  // fold > 0
         const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) oacc[db][qb] *= alpha;
-        const float neg_m = (m_new == -INFINITY ? 0.0f : -m_new) - boff;
+        const float neg_m = m_new == -INFINITY ? 0.0f : -m_new;
         lt[qb] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -557,7 +553,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
   // V descale: fp8 codes, or fp16 values that carry one (the widened codes)
-  const float vsc = a.v_scale ? a.v_scale[hk] : 1.0f;
+  const float vsc = a.v_scale && !a.v_chan ? a.v_scale[hk] : 1.0f;
+  // per-channel descales: output column d is scaled by v_scale[b][hk][d]
+  const float* vch = a.v_chan ? a.v_scale + ((long)b * a.hkv + hk) * D : nullptr;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float l = l_run[qb];
@@ -571,7 +569,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       const int d0 = db * 16 + 4 * g;
-      const v4f o4 = oacc[db][qb] * inv;
+      v4f o4 = oacc[db][qb] * inv;
+      if (vch) o4 *= *reinterpret_cast<const v4f*>(vch + d0);
       u32x2 w;
       if constexpr (O_BF16) {  // hardware round-to-nearest-even
         w[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{o4[0], o4[1]}, v2bf));

@@ -198,34 +198,94 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
 
 // ---------------------------------------------------------------- per-channel mean of K
 // mean[b][h][c] of fp16 x over the tokens of sequence b: the exact sum S of
-// the values (each an integer number of 2^-24 units, accumulated in int64),
-// then fp32(fp64(S) / fp64(L)) * 2^-24; 0 for an empty sequence.  One
-// workgroup per (head, sequence); thread (row group g, channel c).
-constexpr int MEAN_THREADS = 256;
+// the values, then fp32(fp64(S) / fp64(L)) * 2^-24 with S in units of 2^-24;
+// 0 for an empty sequence.  Every fp16 value is an integer number of 2^-24
+// units below 2^40, so a thread's fp64 partial sum of at most MEAN_FLUSH of
+// them stays below 2^53 units and is exact; partials are then added as int64
+// (order-free).  One workgroup per (head, sequence); thread (row group,
+// 16-byte channel chunk); finite inputs.
+constexpr int MEAN_THREADS = 1024;
+constexpr int MEAN_FLUSH = 8192;
 
 template <int DIM>
 __global__ __launch_bounds__(MEAN_THREADS) void k_channel_mean(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int total_tokens,
     float* __restrict__ mean) {
-  constexpr int G = MEAN_THREADS / DIM;  // row groups
+  constexpr int CPR = DIM / 8, G = MEAN_THREADS / CPR;  // chunks per row, row groups
   const int h = blockIdx.x, b = blockIdx.y;
-  const int c = threadIdx.x % DIM, g = threadIdx.x / DIM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = threadIdx.x % CPR, g = threadIdx.x / CPR;
   const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
-  long long acc = 0;
-  for (int t = s0 + g; t < s1; t += G) {
-    const double v = (double)f16_to_f32(x[((long)t * heads + h) * DIM + c]);
-    acc += (long long)(v * 16777216.0);  // exact: an integer below 2^40 in magnitude
-  }
-  __shared__ long long s_acc[MEAN_THREADS];
-  s_acc[threadIdx.x] = acc;
-  __syncthreads();
-  if (g == 0) {
-    long long tot = acc;
+  long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (long c0 = s0 + g; c0 < s1; c0 += (long)G * MEAN_FLUSH) {
+    const long cend = min((long)s1, c0 + (long)G * MEAN_FLUSH);
+    double part[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
+#pragma unroll 4
+    for (long t = c0; t < cend; t += G) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (t * heads + h) * DIM + col * 8);
 #pragma unroll
-    for (int k = 1; k < G; ++k) tot += s_acc[k * DIM + c];
+      for (int e = 0; e < 8; ++e)
+        part[e] += (double)f16_to_f32(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (long long)(part[e] * 16777216.0);  // exact
+  }
+  // lanes lane, lane ^ CPR, lane ^ 2 CPR, ... of a wave hold the same channels
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    for (int off = CPR; off < 64; off <<= 1) acc[e] += __shfl_xor(acc[e], off, 64);
+  __shared__ long long s_acc[MEAN_THREADS / 64][DIM];
+  if (lane < CPR) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_acc[wave][col * 8 + e] = acc[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < DIM; c += MEAN_THREADS) {
+    long long tot = 0;
+    for (int w = 0; w < MEAN_THREADS / 64; ++w) tot += s_acc[w][c];
     const int L = s1 - s0;
     const float m = L > 0 ? (float)((double)tot / (double)L) * 5.9604644775390625e-08f : 0.0f;  // * 2^-24
     mean[((long)b * heads + h) * DIM + c] = m;
+  }
+}
+
+// ---------------------------------------------------------------- per-channel amax
+// max |x| per (sequence, head, channel) as fp32 bit patterns (order-free: a
+// non-negative float compares like its bits), folded into amax_bits
+// [batch, heads, dim] with atomic max.  One workgroup per (CA_TOK tokens,
+// head, sequence); thread (row group, 16-byte channel chunk).
+constexpr int CA_THREADS = 256;
+constexpr int CA_TOK = 256;
+
+template <bool BF16, int DIM>
+__global__ __launch_bounds__(CA_THREADS) void k_channel_amax(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int total_tokens,
+    uint32_t* __restrict__ amax_bits) {
+  constexpr int CPR = DIM / 8, G = CA_THREADS / CPR;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
+  const int t0 = s0 + blockIdx.x * CA_TOK;
+  if (t0 >= s1) return;
+  const int t1 = min(t0 + CA_TOK, s1);
+  const int col = threadIdx.x % CPR, g = threadIdx.x / CPR;
+  uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int t = t0 + g; t < t1; t += G) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + ((long)t * heads + h) * DIM + col * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = h16_to_f32(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu, BF16);
+      m[e] = max(m[e], __float_as_uint(f) & 0x7fffffffu);
+    }
+  }
+  __shared__ uint32_t s_m[G][DIM];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_m[g][col * 8 + e] = m[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < DIM; c += CA_THREADS) {
+    uint32_t r = s_m[0][c];
+    for (int k = 1; k < G; ++k) r = max(r, s_m[k][c]);
+    if (r) atomicMax(amax_bits + ((long)b * heads + h) * DIM + c, r);
   }
 }
 
@@ -240,7 +300,7 @@ constexpr int VP_TILE = 64;
 __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu, int heads, int dim,
     int s_pad, int is_bf16, int total_tokens, int fp8, int wide, const float* __restrict__ descale,
-    void* __restrict__ out) {
+    void* __restrict__ out, int chan = 0) {
   __shared__ uint16_t s_t[128][VP_TILE + 2];  // [d][token], padded rows
   const int t0 = blockIdx.x * VP_TILE, h = blockIdx.y, b = blockIdx.z;
   const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
@@ -259,12 +319,15 @@ __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
     }
   }
   __syncthreads();
-  const float ds = fp8 ? descale[h] : 1.0f;
-  const float rds = 1.0f / ds;
-  const bool fast = ds >= QUOT_MIN_SCALE;  // uniform
+  // chan: one descale per (sequence, head, channel), descale[b][h][d]
+  const float ds_h = fp8 && !chan ? descale[h] : 1.0f;
+  const float rds_h = 1.0f / ds_h;
   const long row_base = ((long)b * heads + h) * dim;
   for (int it = threadIdx.x; it < dim * (VP_TILE / 8); it += VP_THREADS) {
     int d = it / (VP_TILE / 8), p0 = (it % (VP_TILE / 8)) * 8;
+    const float ds = chan ? descale[row_base + d] : ds_h;
+    const float rds = chan ? 1.0f / ds : rds_h;
+    const bool fast = ds >= QUOT_MIN_SCALE;
     int grp = p0 / 32, g = (p0 % 32) / 8;
     uint32_t e16[8];
 #pragma unroll
@@ -388,6 +451,33 @@ bool launch_smooth_quant_int8_block(const void* x, const int32_t* cu, int batch,
   if (dim == 128) hipLaunchKernelGGL((k_quant_int8_block<false, 128, true>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales, mean);
   else hipLaunchKernelGGL((k_quant_int8_block<false, 64, true>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales, mean);
   return hipGetLastError() == hipSuccess;
+}
+
+bool launch_v_permute_per_channel(const void* v, const int32_t* cu, int batch, int heads, int dim,
+                                  int s_pad, bool is_bf16, int total_tokens, bool wide,
+                                  float* descale, void* out, hipStream_t s) {
+  if (batch <= 0) return true;
+  const int n = batch * heads * dim;
+  if (!launch_fill_u32(reinterpret_cast<uint32_t*>(descale), n, 0u, s)) return false;
+  if (s_pad > 0 && total_tokens > 0) {
+    const dim3 grid(s_pad / CA_TOK + (s_pad % CA_TOK != 0), heads, batch);
+    const uint16_t* xp = static_cast<const uint16_t*>(v);
+    uint32_t* ab = reinterpret_cast<uint32_t*>(descale);
+    if (dim == 128) {
+      if (is_bf16) hipLaunchKernelGGL((k_channel_amax<true, 128>), grid, dim3(CA_THREADS), 0, s, xp, cu, heads, total_tokens, ab);
+      else hipLaunchKernelGGL((k_channel_amax<false, 128>), grid, dim3(CA_THREADS), 0, s, xp, cu, heads, total_tokens, ab);
+    } else {
+      if (is_bf16) hipLaunchKernelGGL((k_channel_amax<true, 64>), grid, dim3(CA_THREADS), 0, s, xp, cu, heads, total_tokens, ab);
+      else hipLaunchKernelGGL((k_channel_amax<false, 64>), grid, dim3(CA_THREADS), 0, s, xp, cu, heads, total_tokens, ab);
+    }
+    if (!ok(hipGetLastError())) return false;
+  }
+  if (!launch_finalize_scale(nullptr, descale, n, 448.0f, s)) return false;
+  if (s_pad <= 0) return true;
+  hipLaunchKernelGGL(k_v_permute, dim3(s_pad / VP_TILE, heads, batch), dim3(VP_THREADS), 0, s,
+                     static_cast<const uint16_t*>(v), cu, heads, dim, s_pad, (int)is_bf16,
+                     total_tokens, 1, (int)wide, descale, out, 1);
+  return ok(hipGetLastError());
 }
 
 }  // namespace attnq

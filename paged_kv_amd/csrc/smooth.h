@@ -1,4 +1,5 @@
-// Launch interface of K smoothing before the int8 block quantization (quant.hip).
+// Launch interface of the SageAttention refinements of the quantizers (quant.hip):
+// K smoothing before the int8 block quantization, fp8 V with per-channel descales.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -10,5 +11,12 @@ namespace attnq {
 bool launch_smooth_quant_int8_block(const void* x, const int32_t* cu, int batch, int heads, int dim,
                                     int nblk, int total_tokens, void* codes, float* scales, float* mean,
                                     hipStream_t s);
+
+// descale [batch, heads, dim] fp32 (written: amax over the sequence's tokens
+// / 448, 1 where amax = 0), then V^T as launch_v_permute's fp8 mode with the
+// per-channel descales (wide: each code's fp16 value).
+bool launch_v_permute_per_channel(const void* v, const int32_t* cu, int batch, int heads, int dim,
+                                  int s_pad, bool is_bf16, int total_tokens, bool wide,
+                                  float* descale, void* out, hipStream_t s);
 
 }  // namespace attnq

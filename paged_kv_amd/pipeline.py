@@ -68,7 +68,7 @@ class Fp8Prefill:
     def attend(self):
         A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3,
                               A.FP16 if self.wide_v else A.FP8E4M3, self.qs, self.ks,
-                              self.vs, A.Q_FP8_PER_HEAD, self.cu, self.cu, self.b, self.max_seqlen,
+                              self.vs, A.Q_FP8_PER_HEAD, A.Q_FP8_PER_HEAD, self.cu, self.cu, self.b, self.max_seqlen,
                               self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
                               self.sm_scale, self.causal, self.o, _dtype_code(self.o), self.lse)
 
@@ -86,10 +86,13 @@ class SagePrefill:
     in qs) instead of reading int8 codes written by a separate pass.  With
     smooth_k each sequence's per-channel mean of K (kept in kmean) is
     subtracted before K's int8 quantization (attn_smooth_quant_k): the same
-    softmax output, with lse lower by sm_scale * q . mean."""
+    softmax output, with lse lower by sm_scale * q . mean.  With
+    v_fp8_per_channel V is fp8 e4m3fn with one descale per (sequence, kv head,
+    channel) (kept in vs), stored as the codes' fp16 values; the prefill
+    scales each output column by its channel's descale."""
 
     def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True, want_lse=False,
-                 fuse_q=True, smooth_k=False):
+                 fuse_q=True, smooth_k=False, v_fp8_per_channel=False):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
@@ -99,6 +102,7 @@ class SagePrefill:
         self.sm_scale, self.causal = float(sm_scale), bool(causal)
         self.fuse_q = bool(fuse_q)
         self.smooth_k = bool(smooth_k)
+        self.v_chan = bool(v_fp8_per_channel)
         if self.smooth_k and k.dtype != torch.float16:
             raise TypeError("K smoothing takes fp16 K")
         if v.dtype != torch.float16:
@@ -109,6 +113,7 @@ class SagePrefill:
         self.qs = torch.empty((self.b, self.hq, nblk), dtype=torch.float32, device=dev)
         self.ks = torch.empty((self.b, self.hkv, nblk), dtype=torch.float32, device=dev)
         self.kmean = torch.empty((self.b, self.hkv, self.d), dtype=torch.float32, device=dev) if self.smooth_k else None
+        self.vs = torch.empty((self.b, self.hkv, self.d), dtype=torch.float32, device=dev) if self.v_chan else None
         self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_seqlen, 128)),
                               dtype=torch.float16, device=dev)
         self.o = torch.empty((self.t, self.hq, self.d), dtype=torch.float16, device=dev)
@@ -125,15 +130,16 @@ class SagePrefill:
             A.attn_quant_qk(self.k, _dtype_code(self.k), self.cu, self.b, self.max_seqlen, self.t,
                             self.hkv, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.kc, self.ks)
         A.attn_quant_v_permute(self.v, A.FP16, self.cu, self.b, self.max_seqlen, self.t, self.hkv,
-                               self.d, A.Q_NONE, None, self.vp, None)
+                               self.d, A.Q_FP8_PER_CHANNEL_WIDE if self.v_chan else A.Q_NONE, None,
+                               self.vp, self.vs)
 
     def attend(self):
         if self.fuse_q:
             q, qk_dtype, mode = self.q, _dtype_code(self.q), A.Q_INT8_PER_BLOCK_RAW_Q
         else:
             q, qk_dtype, mode = self.qc, A.INT8, A.Q_INT8_PER_BLOCK
-        A.attn_prefill_varlen(q, self.kc, self.vp, qk_dtype, A.FP16, self.qs, self.ks, None,
-                              mode, self.cu, self.cu, self.b, self.max_seqlen,
+        A.attn_prefill_varlen(q, self.kc, self.vp, qk_dtype, A.FP16, self.qs, self.ks, self.vs,
+                              A.Q_FP8_PER_CHANNEL if self.v_chan else A.Q_FP8_PER_HEAD, mode, self.cu, self.cu, self.b, self.max_seqlen,
                               self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
                               self.sm_scale, self.causal, self.o, A.FP16, self.lse)
 
@@ -222,7 +228,7 @@ class PagedPrefill:
 
     def attend(self):
         A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3, A.FP16, self.qs, self.ks, self.vs,
-                              A.Q_FP8_PER_HEAD, self.cu_q, self.cu_k, self.b, self.max_q, self.max_k,
+                              A.Q_FP8_PER_HEAD, A.Q_FP8_PER_HEAD, self.cu_q, self.cu_k, self.b, self.max_q, self.max_k,
                               self.tq, self.tk, self.hq, self.hkv, self.d, self.sm_scale, self.causal,
                               self.o, _dtype_code(self.o), self.lse)
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert pk.abi_version() == 1
+    assert pk.abi_version() == 2
 
 
 def _err():
@@ -69,6 +69,11 @@ def test_v_permute_validation():
                                   None) == -1
     assert "v_scales" in _err()
     assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, 7, None, FAKE, FAKE, None) != 0
+    # per-channel modes: no per-head amax_in, a descale buffer is required
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_FP8_PER_CHANNEL, FAKE, FAKE, FAKE,
+                                  None) == -1 and "amax_in" in _err()
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 64, pk.Q_FP8_PER_CHANNEL_WIDE, None, FAKE, None,
+                                  None) == -1 and "v_scales" in _err()
 
 
 def test_append_validation():
@@ -88,13 +93,16 @@ def test_append_validation():
 
 def _prefill(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qk=pk.FP8E4M3, vd=pk.FP8E4M3, qs=FAKE, ks=FAKE, vs=FAKE,
-             mode=pk.Q_FP8_PER_HEAD, cq=FAKE, ck=FAKE, b=1, mq=8, mk=8, tq=8, tk=8, hq=4, hkv=2,
+             vmode=pk.Q_FP8_PER_HEAD, mode=pk.Q_FP8_PER_HEAD, cq=FAKE, ck=FAKE, b=1, mq=8, mk=8, tq=8, tk=8, hq=4, hkv=2,
              d=128, sc=0.1, causal=1, o=FAKE, od=pk.BF16, lse=None, st=None)
     a.update(kw)
     return pk.lib().attn_prefill_varlen(*a.values())
 
 
 def test_prefill_validation():
+    assert _prefill(vmode=pk.Q_INT8_PER_BLOCK) == -1 and "v_scale_mode" in _err()
+    assert _prefill(vmode=pk.Q_FP8_PER_CHANNEL, vd=pk.FP16, vs=None) == -1 and "v_scale" in _err()
+    assert _prefill(vmode=pk.Q_FP8_PER_CHANNEL, vs=FAKE + 4) == -1 and "aligned" in _err()
     assert _prefill(hq=3, hkv=2) == -1 and "multiple" in _err()
     assert _prefill(d=96) == -2
     assert _prefill(qk=pk.INT8) == -2            # int8 codes need per-block scales
