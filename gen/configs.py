@@ -310,13 +310,16 @@ def config3() -> dict:
 # ---------------------------------------------------------------------------
 def sparse_mla_inputs(seed: int, batch: int, s_q: int, heads: int, kv_len,
                       block_size: int, topk: int, n_valid=None,
-                      spare_blocks: int = 0) -> dict:
-    """bf16 queries [B,S_q,H,576]; combined int8 cache rows
+                      spare_blocks: int = 0, kv_dtype: str = "int8",
+                      sparse_block_size: int = 1) -> dict:
+    """bf16 queries [B,S_q,H,576]; combined cache rows
     [num_blocks, block_size, 1, 656]; block_table [B, max_blocks];
     sparse_indices [B, S_q, 1, topk] with the n_valid (default topk) valid,
-    distinct, unsorted token indices first and -1 after.
+    distinct, unsorted indices first and -1 after.  An index names the
+    sparse_block_size tokens [idx * sbs, idx * sbs + sbs) (sbs = 1: one token).
 
-    Selected rows hold int8 codes drawn from a rounded normal, bf16 N(0,1)
+    Selected rows hold nope codes (int8: a rounded normal; fp8 e4m3: random
+    sign, exponent field 0..8 and mantissa, so |value| <= 3.75), bf16 N(0,1)
     rope values and positive fp32 tile scales; every other row holds NaN
     rope values and NaN scales, which must never reach an output."""
     rng = np.random.default_rng(seed)
@@ -340,20 +343,35 @@ def sparse_mla_inputs(seed: int, batch: int, s_q: int, heads: int, kv_len,
     cache = np.empty((nb, block_size, 1, MLA_ROW_BYTES), np.uint8)
     cache[...] = tmpl
     nvalid = topk if n_valid is None else n_valid
+    sbs = int(sparse_block_size)
     idx = np.full((batch, s_q, 1, topk), -1, np.int32)
     for b in range(batch):
+        nsb = (int(kv_len[b]) + sbs - 1) // sbs       # sparse blocks holding a token
         for s in range(s_q):
-            k = min(int(nvalid), int(kv_len[b]))
+            k = min(int(nvalid), nsb)
             if k > 0:
-                idx[b, s, 0, :k] = rng.choice(int(kv_len[b]), size=k, replace=False)
-    sel = np.unique(np.concatenate([
-        (table[b][idx[b][idx[b] >= 0] // block_size].astype(np.int64) * block_size
-         + idx[b][idx[b] >= 0] % block_size) for b in range(batch)])) if batch else np.zeros(0, np.int64)
+                idx[b, s, 0, :k] = rng.choice(nsb, size=k, replace=False)
+    toks = []
+    for b in range(batch):
+        t = (idx[b][idx[b] >= 0].astype(np.int64)[:, None] * sbs + np.arange(sbs)[None, :]).ravel()
+        t = t[t < kv_len[b]]
+        toks.append(table[b][t // block_size].astype(np.int64) * block_size + t % block_size)
+    sel = np.unique(np.concatenate(toks)) if batch else np.zeros(0, np.int64)
     rows = cache.reshape(nb * block_size, MLA_ROW_BYTES)
     n = sel.size
-    codes = np.clip(np.rint(rng.standard_normal((n, MLA_NOPE)) * (127.0 / 3.5)), -127, 127).astype(np.int8)
-    rope = bf16_bits(_normal_f32(rng, (n, MLA_ROPE)))
-    scales = (rng.uniform(2.8, 4.2, size=(n, MLA_NOPE // MLA_TILE)) / 127.0).astype(np.float32)
+    if kv_dtype == "int8":
+        codes = np.clip(np.rint(rng.standard_normal((n, MLA_NOPE)) * (127.0 / 3.5)), -127, 127).astype(np.int8)
+        rope = bf16_bits(_normal_f32(rng, (n, MLA_ROPE)))
+        scales = (rng.uniform(2.8, 4.2, size=(n, MLA_NOPE // MLA_TILE)) / 127.0).astype(np.float32)
+    elif kv_dtype == "fp8":
+        sign = rng.integers(0, 2, size=(n, MLA_NOPE)) << 7
+        expo = rng.integers(0, 9, size=(n, MLA_NOPE)) << 3
+        mant = rng.integers(0, 8, size=(n, MLA_NOPE))
+        codes = (sign | expo | mant).astype(np.uint8)
+        rope = bf16_bits(_normal_f32(rng, (n, MLA_ROPE)))
+        scales = rng.uniform(0.5, 1.0, size=(n, MLA_NOPE // MLA_TILE)).astype(np.float32)
+    else:
+        raise ValueError(kv_dtype)
     rows[sel, :MLA_NOPE] = codes.view(np.uint8)
     rows[sel, MLA_NOPE:MLA_NOPE + 2 * MLA_ROPE] = rope.view(np.uint8)
     rows[sel, MLA_NOPE + 2 * MLA_ROPE:] = scales.view(np.uint8)
@@ -361,7 +379,7 @@ def sparse_mla_inputs(seed: int, batch: int, s_q: int, heads: int, kv_len,
         "q": q, "kv_cache": cache, "block_table": table, "max_blocks_per_seq": table.shape[1],
         "kv_lens": kv_len.astype(np.int32), "sparse_indices": idx, "topk": topk,
         "batch": batch, "s_q": s_q, "heads": heads, "num_blocks": nb,
-        "block_size": block_size,
+        "block_size": block_size, "kv_dtype": kv_dtype, "sparse_block_size": sbs,
     }
 
 

@@ -233,22 +233,49 @@ def decode_paged(q_bits, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indic
 # ---------------------------------------------------------------------------
 # sparse MLA-absorb decode
 # ---------------------------------------------------------------------------
-def mla_decode_row(row: np.ndarray):
-    """One 656-byte cache row -> (k_nope fp64 [512], rope fp64 [64])."""
-    codes = row[:MLA_NOPE].view(np.int8).astype(np.float64)
+def mla_decode_row(row: np.ndarray, kv_dtype: str = "int8"):
+    """One 656-byte cache row -> (k_nope fp64 [512], rope fp64 [64]); the
+    nope codes are int8 or fp8 e4m3fn (Ascend "KvQuantSparseFlashAttention",
+    parameter table: key in FLOAT8_E4M3 or INT8)."""
+    if kv_dtype == "int8":
+        codes = row[:MLA_NOPE].view(np.int8).astype(np.float64)
+    elif kv_dtype == "fp8":
+        codes = e4m3fn_decode(row[:MLA_NOPE])
+    else:
+        raise ValueError(kv_dtype)
     rope = bf16_bits_to_f64(row[MLA_NOPE:MLA_NOPE + 2 * MLA_ROPE].view(np.uint16))
     scales = row[MLA_NOPE + 2 * MLA_ROPE:MLA_ROW].view(np.float32).astype(np.float64)
     return codes * np.repeat(scales, MLA_TILE), rope
 
 
+def sparse_mla_tokens(entries, kv_len: int, s: int, s_q: int, sparse_block_size: int = 1,
+                      sparse_mode: int = 0) -> np.ndarray:
+    """The token positions one query row attends to (Ascend
+    "KvQuantSparseFlashAttention", parameters sparse_indices,
+    sparse_block_size, sparse_mode).  Reading: an entry idx >= 0 names the
+    sparse_block_size tokens [idx * sbs, idx * sbs + sbs) (tokens of a block
+    share its selection); a token is used iff it is below kv_len and, with
+    sparse_mode 3 (the lower triangle bounded by the line through the
+    bottom-right corner), at most kv_len - s_q + s for query row s.  Negative
+    entries are padding; every used occurrence is one softmax term."""
+    ent = np.asarray(entries, np.int64)
+    ent = ent[ent >= 0]
+    tok = (ent[:, None] * sparse_block_size + np.arange(sparse_block_size)[None, :]).ravel()
+    lim = kv_len if sparse_mode == 0 else kv_len - s_q + s + 1
+    return tok[tok < lim]
+
+
 def sparse_mla_decode(q_bits, kv_cache, block_table, kv_lens, sparse_indices, sm_scale,
-                      batches=None):
+                      batches=None, kv_dtype: str = "int8", sparse_block_size: int = 1,
+                      sparse_mode: int = 0):
     """q bf16 bits [B, Sq, H, 576]; kv_cache uint8 [NB, bs, 1, 656];
     block_table [B, *]; kv_lens [B]; sparse_indices [B, Sq, 1, topk].
 
-    An index is valid iff 0 <= idx < kv_lens[b]; every valid occurrence is one
+    The tokens of query row (b, s) are sparse_mla_tokens(...); every one is a
     softmax term.  K = [k_nope | rope] (576-d), V = k_nope (512-d).
     Returns o_exact [B,Sq,H,512], o, o_store, lse fp32 [B,Sq,H]."""
+    if sparse_mode not in (0, 3):
+        raise ValueError(sparse_mode)
     q = bf16_bits_to_f64(q_bits)
     nb, sq, h, _ = q.shape
     bs = kv_cache.shape[1]
@@ -257,8 +284,8 @@ def sparse_mla_decode(q_bits, kv_cache, block_table, kv_lens, sparse_indices, sm
     lse = np.full((nb, sq, h), -np.inf)
     for b in (range(nb) if batches is None else batches):
         for s in range(sq):
-            idx = np.asarray(sparse_indices[b, s, 0], np.int64)
-            idx = idx[(idx >= 0) & (idx < int(kv_lens[b]))]
+            idx = sparse_mla_tokens(sparse_indices[b, s, 0], int(kv_lens[b]), s, sq, sparse_block_size,
+                                    sparse_mode)
             n = idx.size
             if n == 0:
                 continue
@@ -266,7 +293,7 @@ def sparse_mla_decode(q_bits, kv_cache, block_table, kv_lens, sparse_indices, sm
             kn = np.empty((n, MLA_NOPE))
             kr = np.empty((n, MLA_ROPE))
             for i in range(n):
-                kn[i], kr[i] = mla_decode_row(rows[r[i]])
+                kn[i], kr[i] = mla_decode_row(rows[r[i]], kv_dtype)
             kd = np.concatenate([kn, kr], axis=1)               # [n, 576]
             o, l = attend(q[b, s], kd, kn, sm_scale, np.full(h, n))
             o_ex[b, s], lse[b, s] = o, l

@@ -183,8 +183,11 @@ def decode_paged(q_bits, k_cache, v_cache, k_scale, v_scale, indptr, indices, la
     return o, lse
 
 
-def sparse_mla(q_bits, kv_cache, block_table, kv_lens, sparse_indices, scale):
-    """Scalar sparse MLA decode; rows parsed with struct."""
+def sparse_mla(q_bits, kv_cache, block_table, kv_lens, sparse_indices, scale, kv_dtype="int8",
+               sparse_block_size=1, sparse_mode=0):
+    """Scalar sparse MLA decode; rows parsed with struct.  Entry e >= 0 covers
+    tokens e*sbs .. e*sbs+sbs-1; a token counts if it is below kv_len and
+    (sparse_mode 3) not past kv_len - s_q + s."""
     b_, sq, h, dq = q_bits.shape
     bs = kv_cache.shape[1]
     o = np.zeros((b_, sq, h, 512))
@@ -192,13 +195,24 @@ def sparse_mla(q_bits, kv_cache, block_table, kv_lens, sparse_indices, scale):
     for b in range(b_):
         for s in range(sq):
             keys, vals = [], []
-            for idx in sparse_indices[b, s, 0]:
-                idx = int(idx)
-                if idx < 0 or idx >= int(kv_lens[b]):
+            toks = []
+            for e in sparse_indices[b, s, 0]:
+                e = int(e)
+                if e < 0:
+                    continue
+                for j in range(sparse_block_size):
+                    toks.append(e * sparse_block_size + j)
+            for idx in toks:
+                if idx >= int(kv_lens[b]):
+                    continue
+                if sparse_mode == 3 and idx > int(kv_lens[b]) - sq + s:
                     continue
                 blk = int(block_table[b][idx // bs])
                 raw = bytes(kv_cache[blk, idx % bs, 0])
-                codes = struct.unpack("<512b", raw[:512])
+                if kv_dtype == "fp8":
+                    codes = [e4m3fn_value(c) for c in raw[:512]]
+                else:
+                    codes = struct.unpack("<512b", raw[:512])
                 rope = [bf16_value(x) for x in struct.unpack("<64H", raw[512:640])]
                 sc = struct.unpack("<4f", raw[640:656])
                 nope = [codes[c] * sc[c // 128] for c in range(512)]

@@ -355,3 +355,72 @@ def test_k_smoothing_leaves_softmax_output_unchanged():
             for h in range(4):
                 shift = 0.3 * float(q[i, h] @ means[b][h // 2])
                 assert abs(float(a["lse"][h, i]) - float(s["lse"][h, i]) - shift) < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# sparse MLA variants: fp8 rows, block-wise sparsity, right-down causal mask
+# ---------------------------------------------------------------------------
+def _mla_var(x, idx=None, **kw):
+    return sparse_mla_decode(x["q"], x["kv_cache"], x["block_table"], x["kv_lens"],
+                             x["sparse_indices"] if idx is None else idx, 1 / 24,
+                             kv_dtype=x["kv_dtype"], sparse_block_size=x["sparse_block_size"], **kw)
+
+
+@pytest.mark.parametrize("kv_dtype", ["int8", "fp8"])
+@pytest.mark.parametrize("sbs", [1, 4])
+@pytest.mark.parametrize("mode", [0, 3])
+def test_mla_variants_vs_brute(kv_dtype, sbs, mode):
+    x = gen.sparse_mla_inputs(21, 2, 3, 2, [40, 25], 16, 5, n_valid=4, spare_blocks=1,
+                              kv_dtype=kv_dtype, sparse_block_size=sbs)
+    idx = x["sparse_indices"].copy()
+    idx[0, 1, 0, 4] = idx[0, 1, 0, 0]            # a duplicate entry counts twice
+    r = _mla_var(x, idx, sparse_mode=mode)
+    bo, bl = brute.sparse_mla(x["q"], x["kv_cache"], x["block_table"], x["kv_lens"], idx, 1 / 24,
+                              kv_dtype=kv_dtype, sparse_block_size=sbs, sparse_mode=mode)
+    assert np.allclose(r["o_exact"], bo, rtol=1e-11, atol=1e-12)
+    assert np.array_equal(np.isinf(r["lse"]), np.isinf(bl))
+    fin = np.isfinite(bl)
+    assert np.allclose(r["lse"][fin], bl[fin], rtol=1e-6)
+    assert not np.isnan(r["o_exact"]).any()
+
+
+def test_mla_block_sparse_is_its_token_expansion():
+    # an entry e of block size 4 is the four token entries 4e .. 4e+3
+    x = gen.sparse_mla_inputs(22, 2, 1, 2, [40, 25], 16, 4, n_valid=3, sparse_block_size=4)
+    idx = x["sparse_indices"]
+    tok = np.where(idx[..., None] >= 0, idx[..., None] * 4 + np.arange(4), -1).reshape(2, 1, 1, 16)
+    a = _mla_var(x)
+    y = dict(x, sparse_block_size=1)
+    b = _mla_var(y, tok)
+    assert np.array_equal(a["o_exact"], b["o_exact"]) and np.array_equal(a["lse"], b["lse"])
+
+
+def test_mla_right_down_causal():
+    x = gen.sparse_mla_inputs(23, 2, 4, 2, [40, 25], 16, 12, n_valid=10)
+    kv = x["kv_lens"]
+    full = _mla_var(x)
+    causal = _mla_var(x, sparse_mode=3)
+    for b in range(2):
+        for s in range(4):
+            # row s keeps exactly the tokens at or before kv_len - 4 + s
+            idx = x["sparse_indices"].copy()
+            row = idx[b, s, 0]
+            row[row > kv[b] - 4 + s] = -1
+            one = _mla_var(x, idx)
+            assert np.array_equal(causal["o_exact"][b, s], one["o_exact"][b, s])
+    # the last query row sees every token below kv_len: no mask
+    assert np.array_equal(causal["o_exact"][:, 3], full["o_exact"][:, 3])
+    # with one query row the mask removes nothing
+    y = gen.sparse_mla_inputs(23, 2, 1, 2, [40, 25], 16, 12, n_valid=10)
+    assert np.array_equal(_mla_var(y, sparse_mode=3)["o_exact"], _mla_var(y)["o_exact"])
+
+
+def test_mla_fp8_row_decode():
+    from oracle.attention import mla_decode_row
+    x = gen.sparse_mla_inputs(24, 1, 1, 1, 16, 16, 16, kv_dtype="fp8")
+    row = x["kv_cache"][x["block_table"][0][0], 3, 0]
+    kn, kr = mla_decode_row(row, "fp8")
+    sc = row[640:656].view(np.float32)
+    for c in range(512):
+        assert kn[c] == brute.e4m3fn_value(int(row[c])) * float(sc[c // 128])
+    assert np.abs(kn).max() <= 3.75 * float(sc.max())
