@@ -261,28 +261,37 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       size_t workspace_bytes, void* o, float* lse, hipStream_t stream);
 
 /*
- * attn_sparse_mla_decode -- MLA-absorb sparse attention over int8 cache rows
- * with per-token tile-128 scales (Ascend "KvQuantSparseFlashAttention":
+ * attn_sparse_mla_decode -- MLA-absorb sparse attention over int8 or fp8 cache
+ * rows with per-token tile-128 scales (Ascend "KvQuantSparseFlashAttention":
  * attention_mode 2, quant_scale_repo_mode 1, tile_size 128, rope_head_dim 64,
- * PA_BSND paging, sparse_block_size 1, sparse_mode 0).
+ * PA_BSND paging, key/value FLOAT8_E4M3 or INT8, sparse_block_size,
+ * sparse_mode 0 or 3).
  *   q bf16 [batch, s_q, num_heads, 576] = [q_nope 512 | q_rope 64].
  *   kv_cache uint8 [num_blocks, block_size, 1, 656]; each 656-byte row is
- *     512 int8 nope codes | 64 bf16 rope values | 4 fp32 scales (scale t covers
- *     nope channels [128t, 128t+128)).  K = [codes*scale | rope], V = codes*scale.
+ *     512 nope codes (kv_dtype INT8: int8; FP8E4M3: e4m3fn) | 64 bf16 rope values |
+ *     4 fp32 scales (scale t covers nope channels [128t, 128t+128)).
+ *     K = [codes*scale | rope], V = codes*scale.
  *   block_table int32 [batch, max_blocks_per_seq]: token i of sequence b is row
  *     i % block_size of block block_table[b][i / block_size].
- *   kv_lens int32 [batch]; sparse_indices int32 [batch, s_q, 1, topk]: an entry is
- *     used iff 0 <= idx < kv_lens[b] (valid entries first, -1 padding after);
- *     each used entry is one softmax term.
+ *   kv_lens int32 [batch]; sparse_indices int32 [batch, s_q, 1, topk]: an entry
+ *     e >= 0 names the sparse_block_size tokens [e*sbs, e*sbs + sbs) (tokens of a
+ *     block share its selection; -1 padding after the valid entries); a named
+ *     token is used iff it is below kv_lens[b] and, with sparse_mode 3 (the
+ *     right-down causal mask), at most kv_lens[b] - s_q + s for query row s.
+ *     Each used token is one softmax term (an entry given twice counts twice).
+ *   sparse_block_size in {1, 2, 4, 8, 16} (so it divides block_size).
  *   o bf16 [batch, s_q, num_heads, 512]; lse optional fp32 [batch, s_q, num_heads];
- *   rows with no used entry get o = 0 and lse = -inf.
+ *   rows with no used token get o = 0 and lse = -inf.
  *   num_heads in {1,2,4,8,16,32,48,64,128}; block_size a multiple of 16, <= 1024;
- *   topk > 0.  workspace >= attn_sparse_mla_decode_workspace_size(...).
+ *   topk > 0.  workspace >= attn_sparse_mla_decode_workspace_size(...) bytes,
+ *   256-byte aligned (0 is returned for invalid sizes).
  */
-size_t attn_sparse_mla_decode_workspace_size(int batch, int s_q, int num_heads, int topk);
-int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
-                           int max_blocks_per_seq, const int32_t* kv_lens,
-                           const int32_t* sparse_indices, int topk, int batch, int s_q,
+size_t attn_sparse_mla_decode_workspace_size(int batch, int s_q, int num_heads, int topk,
+                                             int sparse_block_size);
+int attn_sparse_mla_decode(const void* q, const void* kv_cache, int kv_dtype,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* kv_lens, const int32_t* sparse_indices, int topk,
+                           int sparse_block_size, int sparse_mode, int batch, int s_q,
                            int num_heads, int num_blocks, int block_size, float sm_scale,
                            void* workspace, size_t workspace_bytes, void* o, float* lse,
                            hipStream_t stream);

@@ -47,8 +47,8 @@ SYMBOLS = {
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                _P, _Z, _P, _P, _P]),
-    "attn_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
-    "attn_sparse_mla_decode": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
+    "attn_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_sparse_mla_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
                                     _P, _P, _P]),
 }
 
@@ -181,16 +181,17 @@ def attn_decode_paged(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indic
                                    _ptr(lse), s), "attn_decode_paged")
 
 
-def attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk) -> int:
-    return int(lib().attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk))
+def attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk, sparse_block_size=1) -> int:
+    return int(lib().attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk, sparse_block_size))
 
 
-def attn_sparse_mla_decode(q, kv_cache, block_table, max_blocks_per_seq, kv_lens, sparse_indices,
-                           topk, batch, s_q, num_heads, num_blocks, block_size, sm_scale,
-                           workspace, workspace_bytes, o, lse=None, stream=None):
+def attn_sparse_mla_decode(q, kv_cache, kv_dtype, block_table, max_blocks_per_seq, kv_lens, sparse_indices,
+                           topk, sparse_block_size, sparse_mode, batch, s_q, num_heads, num_blocks,
+                           block_size, sm_scale, workspace, workspace_bytes, o, lse=None, stream=None):
     s = _stream(stream, q, o)
-    _check(lib().attn_sparse_mla_decode(_ptr(q), _ptr(kv_cache), _ptr(block_table),
+    _check(lib().attn_sparse_mla_decode(_ptr(q), _ptr(kv_cache), kv_dtype, _ptr(block_table),
                                         max_blocks_per_seq, _ptr(kv_lens), _ptr(sparse_indices),
-                                        topk, batch, s_q, num_heads, num_blocks, block_size,
+                                        topk, sparse_block_size, sparse_mode, batch, s_q, num_heads,
+                                        num_blocks, block_size,
                                         float(sm_scale), _ptr(workspace), int(workspace_bytes),
                                         _ptr(o), _ptr(lse), s), "attn_sparse_mla_decode")

@@ -10,6 +10,7 @@
 #include "launch.h"
 #include "gather.h"
 #include "smooth.h"
+#include "mla.h"
 
 namespace {
 
@@ -378,22 +379,33 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
 }
 
 // ---------------------------------------------------------------- attn_sparse_mla_decode
-size_t attn_sparse_mla_decode_workspace_size(int batch, int s_q, int num_heads, int topk) {
-  if (batch <= 0 || s_q <= 0 || num_heads <= 0 || topk <= 0) return 0;
-  return attnq::mla_workspace_bytes(batch, s_q, num_heads, topk);
+static bool mla_sbs_ok(int sbs) { return sbs == 1 || sbs == 2 || sbs == 4 || sbs == 8 || sbs == 16; }
+
+size_t attn_sparse_mla_decode_workspace_size(int batch, int s_q, int num_heads, int topk,
+                                             int sparse_block_size) {
+  if (batch <= 0 || s_q <= 0 || num_heads <= 0 || topk <= 0 || !mla_sbs_ok(sparse_block_size)) return 0;
+  if ((long)topk * sparse_block_size > 0x7FFFFFFFL) return 0;
+  return attnq::mla_workspace_bytes(batch, s_q, num_heads, topk * sparse_block_size);
 }
 
-int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+int attn_sparse_mla_decode(const void* q, const void* kv_cache, int kv_dtype, const int32_t* block_table,
                            int max_blocks_per_seq, const int32_t* kv_lens,
-                           const int32_t* sparse_indices, int topk, int batch, int s_q,
-                           int num_heads, int num_blocks, int block_size, float sm_scale,
-                           void* workspace, size_t workspace_bytes, void* o, float* lse,
-                           hipStream_t stream) {
+                           const int32_t* sparse_indices, int topk, int sparse_block_size,
+                           int sparse_mode, int batch, int s_q, int num_heads, int num_blocks,
+                           int block_size, float sm_scale, void* workspace, size_t workspace_bytes,
+                           void* o, float* lse, hipStream_t stream) {
   static const int kHeads[] = {1, 2, 4, 8, 16, 32, 48, 64, 128};
   bool heads_ok = false;
   for (int h : kHeads) heads_ok |= (h == num_heads);
   REQUIRE(heads_ok, ATTNQ_EUNSUPPORTED, "num_heads must be one of 1,2,4,8,16,32,48,64,128 (got %d)", num_heads);
   REQUIRE(topk > 0, ATTNQ_EINVAL, "topk must be > 0 (got %d)", topk);
+  REQUIRE(kv_dtype == ATTNQ_INT8 || kv_dtype == ATTNQ_FP8E4M3, ATTNQ_EUNSUPPORTED,
+          "kv_dtype must be INT8 or FP8E4M3 (got %d)", kv_dtype);
+  REQUIRE(mla_sbs_ok(sparse_block_size), ATTNQ_EUNSUPPORTED,
+          "sparse_block_size must be 1, 2, 4, 8 or 16 (got %d)", sparse_block_size);
+  REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTNQ_EUNSUPPORTED, "sparse_mode must be 0 or 3 (got %d)",
+          sparse_mode);
+  REQUIRE((long)topk * sparse_block_size <= 0x7FFFFFFFL, ATTNQ_EINVAL, "topk * sparse_block_size too large");
   REQUIRE(block_size >= 16 && block_size <= 1024 && block_size % 16 == 0, ATTNQ_EINVAL,
           "block_size must be a multiple of 16 in [16, 1024] (got %d)", block_size);
   REQUIRE(batch >= 0 && s_q >= 0, ATTNQ_EINVAL, "batch and s_q must be >= 0");
@@ -408,7 +420,7 @@ int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* b
   REQUIRE_PTR(o, 16);
   REQUIRE_OPT_PTR(lse, 4);
   REQUIRE_PTR(workspace, 256);
-  const size_t need = attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk);
+  const size_t need = attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk, sparse_block_size);
   REQUIRE(workspace_bytes >= need, ATTNQ_EWORKSPACE, "workspace too small: %zu < %zu bytes",
           workspace_bytes, need);
   attnq::MlaArgs a;
@@ -418,12 +430,13 @@ int attn_sparse_mla_decode(const void* q, const void* kv_cache, const int32_t* b
   a.o = o; a.lse = lse;
   a.batch = batch; a.s_q = s_q; a.heads = num_heads; a.num_blocks = num_blocks;
   a.block_size = block_size; a.max_blocks = max_blocks_per_seq; a.topk = topk;
-  a.n_split = attnq::mla_n_split(topk);
+  a.n_split = attnq::mla_n_split(topk * sparse_block_size);
   const size_t rows = (size_t)batch * s_q * a.n_split * num_heads;
   a.ws_o = static_cast<uint16_t*>(workspace);
   a.ws_lse = reinterpret_cast<float*>(a.ws_o + rows * 512);
   a.sm_scale_log2 = sm_scale * LOG2E;
-  LAUNCHED(attnq::launch_mla(a, stream));
+  const attnq::MlaMode m{kv_dtype == ATTNQ_FP8E4M3 ? 1 : 0, sparse_block_size, sparse_mode};
+  LAUNCHED(attnq::launch_mla_mode(a, m, stream));
   return ok();
 }
 

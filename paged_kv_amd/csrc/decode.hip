@@ -274,11 +274,11 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
   if (n < G) {
     const int qh = hk * G + n;
     const long row = ((long)b * a.hq + qh) * a.n_chunks + chunk;
-    const float inv = l > 0.f ? vsc / l : 0.f;
+    const float inv = l != 0.f ? vsc / l : 0.f;  // a NaN sum stays NaN
 #pragma unroll
     for (int db = 0; db < DEC_D / 16; ++db)
       *reinterpret_cast<v4f*>(a.ws_o + row * DEC_D + db * 16 + 4 * g) = oacc[db] * inv;
-    if (g == 0) a.ws_lse[row] = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
+    if (g == 0) a.ws_lse[row] = l != 0.f ? m_ref + __log2f(l) : -INFINITY;
   }
 }
 
@@ -304,12 +304,17 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(const DecodeArgs
   const int kv_len = npg > 0 ? (npg - 1) * a.page_size + clampi(a.kv_last[b], 0, a.page_size) : 0;
   const int nc = min(a.n_chunks, (kv_len + DEC_CHUNK_TOKENS - 1) / DEC_CHUNK_TOKENS);
   const long row0 = (long)row * a.n_chunks;
+  // a NaN partial (a NaN value among the used tokens) makes the row NaN
   float m = -INFINITY;
-  for (int c0 = 0; c0 < nc; c0 += 64)
-    m = fmaxf(m, wave_max(c0 + lane < nc ? a.ws_lse[row0 + c0 + lane] : -INFINITY));
+  bool nan = false;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const float lc = c0 + lane < nc ? a.ws_lse[row0 + c0 + lane] : -INFINITY;
+    nan |= __ballot(lc != lc) != 0;
+    m = fmaxf(m, wave_max(lc));
+  }
   float tot = 0.f;
   v2f acc = v2f{0.f, 0.f};
-  if (m != -INFINITY) {
+  if (m != -INFINITY && !nan) {
     for (int c0 = 0; c0 < nc; c0 += 64) {
       const float lc = c0 + lane < nc ? a.ws_lse[row0 + c0 + lane] : -INFINITY;
       const float w = lc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lc - m);
@@ -329,10 +334,11 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(const DecodeArgs
                *reinterpret_cast<const v2f*>(op + (long)c * DEC_D);
     }
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const float inv = nan ? __builtin_nanf("") : tot > 0.f ? 1.f / tot : 0.f;
   const v2bf ob = __builtin_convertvector(acc * inv, v2bf);
   *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.o) + (long)row * DEC_D + 2 * lane) = __builtin_bit_cast(uint32_t, ob);
-  if (a.lse && lane == 0) a.lse[row] = tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
+  if (a.lse && lane == 0)
+    a.lse[row] = nan ? __builtin_nanf("") : tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
 }
 
 int decode_chunk_pages(int page_size) { return DEC_CHUNK_TOKENS / page_size; }

@@ -1,15 +1,18 @@
-// MLA-absorb sparse decode over int8 cache rows with per-token tile-128
-// scales (Ascend "KvQuantSparseFlashAttention": attention_mode 2, combined
-// quant-scale rows, PA_BSND paging through block_table, sparse_indices).
+// MLA-absorb sparse decode over int8 or fp8 cache rows with per-token
+// tile-128 scales (Ascend "KvQuantSparseFlashAttention": attention_mode 2,
+// combined quant-scale rows, PA_BSND paging through block_table,
+// sparse_indices, sparse_block_size, sparse_mode 0 or 3).
 //
-// Row format (656 bytes): 512 int8 nope codes | 64 bf16 rope | 4 fp32 scales
-// (scale t covers nope channels [128t, 128t+128)).  K = [codes*scale | rope],
-// V = codes*scale, logit = sm_scale * q . K.
+// Row format (656 bytes): 512 nope codes (int8 or e4m3fn) | 64 bf16 rope |
+// 4 fp32 scales (scale t covers nope channels [128t, 128t+128)).
+// K = [codes*scale | rope], V = codes*scale, logit = sm_scale * q . K.
+// An index entry e >= 0 names tokens [e*sbs, e*sbs + sbs); a token is used
+// if it is below kv_len and, with sparse_mode 3, at most kv_len - s_q + s.
 //
 // Split phase: one workgroup (16 waves) per (query row, 256-index split,
 // group of 64 heads).  The split's indices are resolved through block_table once,
 // into LDS.  Per 32-index step the workgroup gathers the 32 selected rows,
-// widens the int8 codes to fp16 (exact) into token-major LDS rows.  Four
+// widens the codes to fp16 (exact for int8 and e4m3fn) into token-major LDS rows.  Four
 // waves serve 16 heads, split by channel tile: each owns one 128-channel tile
 // of QK and PV (the last one also the rope part) and the four exchange their
 // partial scores through LDS once per step; the PV operand (channel-major)
@@ -27,6 +30,7 @@
 // everything else is exact up to fp32 accumulation.
 #include "kcommon.h"
 #include "launch.h"
+#include "mla.h"
 
 namespace attnq {
 
@@ -84,7 +88,14 @@ ATTNQ_DEV void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
   hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, b) - off);
 }
 
-__global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
+// 4 e4m3fn codes -> 4 fp16 values (every e4m3fn value is exact in fp16).
+ATTNQ_DEV void f8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+template <bool KV_FP8>
+__global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, const MlaMode md) {
   __shared__ __attribute__((aligned(16))) MlaLds L;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,22 +104,30 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, row = blockIdx.y;  // row = b * s_q + s
   const int b = row / a.s_q;
+  const int sbs = md.sparse_block_size;           // a power of 2
+  const int ntok = a.topk * sbs;                  // token slots of the row
   const int e_begin = split * MLA_SPLIT_TOKENS;
-  const int e_end = min(a.topk, e_begin + MLA_SPLIT_TOKENS);
+  const int e_end = min(ntok, e_begin + MLA_SPLIT_TOKENS);
   const int head = blockIdx.z * MLA_WG_HEADS + hb * 16 + n;
   const bool wave_active = blockIdx.z * MLA_WG_HEADS + hb * 16 < a.heads;
 
-  // ---- resolve this split's indices to cache rows once
+  // ---- resolve this split's token slots to cache rows once.  Slot u is
+  // token idx[u / sbs] * sbs + u % sbs; used below `lim`.
   {
     const int kv_len = a.kv_lens[b];
+    const int s = row - b * a.s_q;
+    const int lim = md.sparse_mode == 3 ? kv_len - a.s_q + s + 1 : kv_len;
+    const int sh = __builtin_ctz((unsigned)sbs);
     const int* idx_row = a.idx + (long)row * a.topk;
     for (int e = threadIdx.x; e < MLA_SPLIT_TOKENS; e += MLA_THREADS) {
       int r = -1;
-      if (e_begin + e < e_end) {
-        const int i = idx_row[e_begin + e];
-        if (i >= 0 && i < kv_len && i / a.block_size < a.max_blocks) {
-          const int blk = a.block_table[(long)b * a.max_blocks + i / a.block_size];
-          if (blk >= 0 && blk < a.num_blocks) r = blk * a.block_size + i % a.block_size;
+      const int u = e_begin + e;
+      if (u < e_end) {
+        const int ent = idx_row[u >> sh];
+        const long i = ((long)ent << sh) + (u & (sbs - 1));
+        if (ent >= 0 && i < lim && i / a.block_size < a.max_blocks) {
+          const int blk = a.block_table[(long)b * a.max_blocks + (int)(i / a.block_size)];
+          if (blk >= 0 && blk < a.num_blocks) r = blk * a.block_size + (int)(i % a.block_size);
         }
       }
       L.row_idx[e] = r;
@@ -172,7 +191,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
         if (col < MLA_NOPE) {
           uint32_t h[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) i8x4_to_f16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (KV_FP8) f8x4_to_f16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
+            else i8x4_to_f16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
+          }
           u32x4* dn = reinterpret_cast<u32x4*>(&B.nat[r * NAT_ROW + col]);
           dn[0] = u32x4{h[0], h[1], h[2], h[3]};
           dn[1] = u32x4{h[4], h[5], h[6], h[7]};
@@ -314,7 +336,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
   l += __shfl_xor(l, 32, 64);
   if (head < a.heads) {
     const long prow = ((long)row * a.n_split + split) * a.heads + head;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l != 0.f ? 1.f / l : 0.f;  // a NaN sum stays NaN
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const v4f o4 = oacc[db] * inv;
@@ -322,7 +344,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a) {
       const uint32_t w1 = f32_to_bf16(o4[2]) | (f32_to_bf16(o4[3]) << 16);
       *reinterpret_cast<uint2*>(a.ws_o + prow * MLA_NOPE + 128 * t + db * 16 + 4 * g) = make_uint2(w0, w1);
     }
-    if (g == 0 && t == 0) a.ws_lse[prow] = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
+    if (g == 0 && t == 0) a.ws_lse[prow] = l != 0.f ? m_ref + __log2f(l) : -INFINITY;
   }
 }
 
@@ -331,11 +353,17 @@ __global__ __launch_bounds__(128) void k_mla_merge(const MlaArgs a) {
   const int rh = blockIdx.x;  // row * heads + head
   const int row = rh / a.heads, head = rh % a.heads;
   const int d0 = threadIdx.x * 4;
+  // a NaN partial (a NaN value among the used tokens) makes the row NaN
   float m = -INFINITY;
-  for (int c = 0; c < a.n_split; ++c) m = fmaxf(m, a.ws_lse[((long)row * a.n_split + c) * a.heads + head]);
+  bool nan = false;
+  for (int c = 0; c < a.n_split; ++c) {
+    const float lc = a.ws_lse[((long)row * a.n_split + c) * a.heads + head];
+    nan |= lc != lc;
+    m = fmaxf(m, lc);
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
-  if (m != -INFINITY) {
+  if (m != -INFINITY && !nan) {
     for (int c = 0; c < a.n_split; ++c) {
       const long prow = ((long)row * a.n_split + c) * a.heads + head;
       const float lc = a.ws_lse[prow];
@@ -347,11 +375,12 @@ __global__ __launch_bounds__(128) void k_mla_merge(const MlaArgs a) {
       acc[2] += w * bf16_to_f32(o2.y & 0xffffu); acc[3] += w * bf16_to_f32(o2.y >> 16);
     }
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const float inv = nan ? __builtin_nanf("") : tot > 0.f ? 1.f / tot : 0.f;
   uint32_t w0 = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
   uint32_t w1 = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + (long)rh * MLA_NOPE + d0) = make_uint2(w0, w1);
-  if (a.lse && threadIdx.x == 0) a.lse[rh] = tot > 0.f ? (m + __log2f(tot)) * MLA_LN2 : -INFINITY;
+  if (a.lse && threadIdx.x == 0)
+    a.lse[rh] = nan ? __builtin_nanf("") : tot > 0.f ? (m + __log2f(tot)) * MLA_LN2 : -INFINITY;
 }
 
 int mla_n_split(int topk) { return (topk + MLA_SPLIT_TOKENS - 1) / MLA_SPLIT_TOKENS; }
@@ -361,14 +390,19 @@ size_t mla_workspace_bytes(int batch, int s_q, int heads, int topk) {
   return rows * MLA_NOPE * sizeof(uint16_t) + rows * sizeof(float) + 256;
 }
 
-bool launch_mla(const MlaArgs& a, hipStream_t s) {
+bool launch_mla_mode(const MlaArgs& a, const MlaMode& m, hipStream_t s) {
   const int rows = a.batch * a.s_q;
   if (rows <= 0) return true;
   const int hgroups = (a.heads + MLA_WG_HEADS - 1) / MLA_WG_HEADS;
-  hipLaunchKernelGGL(k_mla_split, dim3(a.n_split, rows, hgroups), dim3(MLA_THREADS), 0, s, a);
+  if (m.kv_fp8)
+    hipLaunchKernelGGL((k_mla_split<true>), dim3(a.n_split, rows, hgroups), dim3(MLA_THREADS), 0, s, a, m);
+  else
+    hipLaunchKernelGGL((k_mla_split<false>), dim3(a.n_split, rows, hgroups), dim3(MLA_THREADS), 0, s, a, m);
   if (hipGetLastError() != hipSuccess) return false;
   hipLaunchKernelGGL(k_mla_merge, dim3(rows * a.heads), dim3(128), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
+
+bool launch_mla(const MlaArgs& a, hipStream_t s) { return launch_mla_mode(a, MlaMode{0, 1, 0}, s); }
 
 }  // namespace attnq

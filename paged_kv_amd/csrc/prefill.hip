@@ -563,7 +563,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     l += __shfl_xor(l, 32, 64);
     const int row = wq0 + qb * 16 + n;
     if (row >= Lq) continue;
-    const bool any = l > 0.0f;
+    const bool any = l != 0.0f;  // a visible key (a NaN sum stays NaN)
     const float inv = any ? vsc / l : 0.0f;
     const long obase = ((long)(q0 + row) * a.hq + h) * D;
 #pragma unroll

@@ -263,23 +263,27 @@ class PagedDecode:
 
 
 class SparseMlaDecode:
-    """MLA-absorb sparse decode over int8 cache rows with tile-128 scales."""
+    """MLA-absorb sparse decode over int8 (or fp8 e4m3, kv_fp8) cache rows with
+    tile-128 scales; an index names sparse_block_size consecutive tokens;
+    sparse_mode 3 adds the right-down causal mask over the s_q query rows."""
 
     def __init__(self, q, kv_cache, block_table, kv_lens, sparse_indices, sm_scale=None,
-                 want_lse=False):
+                 want_lse=False, kv_fp8=False, sparse_block_size=1, sparse_mode=0):
         dev = q.device
         self.q, self.cache, self.table, self.kv_lens, self.idx = q, kv_cache, block_table, kv_lens, sparse_indices
         self.b, self.sq, self.h, dq = q.shape
         self.topk = sparse_indices.shape[-1]
+        self.kv_dtype = A.FP8E4M3 if kv_fp8 else A.INT8
+        self.sbs, self.mode = int(sparse_block_size), int(sparse_mode)
         self.sm_scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(dq)
-        self.ws_bytes = A.attn_sparse_mla_decode_workspace_size(self.b, self.sq, self.h, self.topk)
+        self.ws_bytes = A.attn_sparse_mla_decode_workspace_size(self.b, self.sq, self.h, self.topk, self.sbs)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.o = torch.empty((self.b, self.sq, self.h, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.b, self.sq, self.h), dtype=torch.float32, device=dev) if want_lse else None
 
     def run(self):
-        A.attn_sparse_mla_decode(self.q, self.cache, self.table, self.table.shape[1], self.kv_lens,
-                                 self.idx, self.topk, self.b, self.sq, self.h, self.cache.shape[0],
+        A.attn_sparse_mla_decode(self.q, self.cache, self.kv_dtype, self.table, self.table.shape[1], self.kv_lens,
+                                 self.idx, self.topk, self.sbs, self.mode, self.b, self.sq, self.h, self.cache.shape[0],
                                  self.cache.shape[1], self.sm_scale, self.ws, self.ws_bytes, self.o,
                                  self.lse)
         return self.o

@@ -177,8 +177,8 @@ def test_smooth_quant_k_validation():
 
 
 def _mla(**kw):
-    a = dict(q=FAKE, c=FAKE, bt=FAKE, mb=4, kl=FAKE, idx=FAKE, topk=8, b=1, sq=1, h=16, nb=8, bs=64,
-             sc=0.04, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, st=None)
+    a = dict(q=FAKE, c=FAKE, kvd=pk.INT8, bt=FAKE, mb=4, kl=FAKE, idx=FAKE, topk=8, sbs=1, mode=0, b=1, sq=1,
+             h=16, nb=8, bs=64, sc=0.04, ws=FAKE, wsb=1 << 30, o=FAKE, lse=None, st=None)
     a.update(kw)
     return pk.lib().attn_sparse_mla_decode(*a.values())
 
@@ -189,6 +189,13 @@ def test_mla_validation():
     assert _mla(bs=8) == -1 and "block_size" in _err()
     assert _mla(bs=1040) == -1
     assert _mla(wsb=8) == -3
+    assert _mla(kvd=pk.BF16) == -2 and "kv_dtype" in _err()
+    assert _mla(sbs=3) == -2 and "sparse_block_size" in _err()
+    assert _mla(sbs=32) == -2
+    assert _mla(mode=1) == -2 and "sparse_mode" in _err()
+    L = pk.lib()
+    assert L.attn_sparse_mla_decode_workspace_size(1, 1, 16, 8, 3) == 0
+    assert L.attn_sparse_mla_decode_workspace_size(1, 1, 16, 300, 4) == L.attn_sparse_mla_decode_workspace_size(1, 1, 16, 1200, 1)
 
 
 def test_python_binding_raises_with_message():
