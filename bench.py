@@ -243,6 +243,24 @@ def bench_config4(iters, cpu=False):
          "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12}
     if cpu:
         r["cpu_oracle"] = oracle_config4(x)
+    del p, x
+    torch.cuda.empty_cache()
+    # the variants at the same size (2048 selected rows of 656 bytes per query row):
+    # fp8 e4m3 rows; 128 entries of 16-token blocks
+    for name, kw in (("fp8_rows", dict(kv_dtype="fp8")), ("block_sparse_16", dict(sparse_block_size=16))):
+        topk = 2048 // kw.get("sparse_block_size", 1)
+        y = gen.sparse_mla_inputs(gen.seed_for(4), 32, 1, 128, 65536, 64, topk, **kw)
+        pv = SparseMlaDecode(to_dev(y["q"]), to_dev(y["kv_cache"]), to_dev(y["block_table"]),
+                             to_dev(y["kv_lens"]), to_dev(y["sparse_indices"]), 1.0 / 24.0,
+                             kv_fp8=y["kv_dtype"] == "fp8", sparse_block_size=y["sparse_block_size"])
+        pv.run()
+        torch.cuda.synchronize()
+        settle(pv.run)
+        vms = float(np.median(time_events(pv.run, iters, make_flush())))
+        vbytes = nbytes - 32 * 2048 * 4 + 32 * topk * 4
+        r[name] = {"ms": vms, "GB/s": vbytes / (vms * 1e-3) / 1e9, "pct_hbm": 100 * vbytes / (vms * 1e-3) / 1e9 / PEAK_HBM}
+        del pv, y
+        torch.cuda.empty_cache()
     return r
 
 
