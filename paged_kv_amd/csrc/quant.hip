@@ -205,7 +205,8 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
 // (order-free).  One workgroup per (head, sequence); thread (row group,
 // 16-byte channel chunk); finite inputs.
 constexpr int MEAN_THREADS = 1024;
-constexpr int MEAN_FLUSH = 8192;
+constexpr int MEAN_FLUSH = 8192;  // a multiple of MEAN_BATCH
+constexpr int MEAN_BATCH = 8;
 
 template <int DIM>
 __global__ __launch_bounds__(MEAN_THREADS) void k_channel_mean(
@@ -220,12 +221,20 @@ __global__ __launch_bounds__(MEAN_THREADS) void k_channel_mean(
   for (long c0 = s0 + g; c0 < s1; c0 += (long)G * MEAN_FLUSH) {
     const long cend = min((long)s1, c0 + (long)G * MEAN_FLUSH);
     double part[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
-#pragma unroll 4
-    for (long t = c0; t < cend; t += G) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (t * heads + h) * DIM + col * 8);
+    // MEAN_BATCH rows per thread in flight before they are added
+    for (long t = c0; t < cend; t += (long)G * MEAN_BATCH) {
+      u32x4 v[MEAN_BATCH];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        part[e] += (double)f16_to_f32(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
+      for (int u = 0; u < MEAN_BATCH; ++u) {
+        const long tu = t + (long)u * G;
+        v[u] = tu < cend ? *reinterpret_cast<const u32x4*>(x + (tu * heads + h) * DIM + col * 8)
+                         : u32x4{0u, 0u, 0u, 0u};  // +0 adds nothing
+      }
+#pragma unroll
+      for (int u = 0; u < MEAN_BATCH; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part[e] += (double)f16_to_f32(e & 1 ? v[u][e >> 1] >> 16 : v[u][e >> 1] & 0xffffu);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += (long long)(part[e] * 16777216.0);  // exact
