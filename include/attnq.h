@@ -13,6 +13,12 @@
  *    never allocates, frees, copies to the host or synchronizes: each call
  *    only validates its host arguments and enqueues kernels on `stream`
  *    (0 = the null stream), in order, asynchronously.
+ *  - Capture-safe (FlashInfer "[Refactor] Unify JIT/Customization/AOT
+ *    mode": the decode/prefill plans take enable_cuda_graph; Ascend
+ *    "KvQuantSparseFlashAttention", 约束说明: graph mode): the enqueued work is
+ *    kernels only (scales and counters are cleared by fill kernels, not
+ *    memsets), so a sequence of calls can be recorded into a HIP graph and
+ *    replayed; a replay reads the input buffers as they are at that time.
  *  - Return value: ATTNQ_OK (0) or a negative attnq_status.  On a negative
  *    status nothing was enqueued and attnq_last_error() (thread-local) holds
  *    a message.
