@@ -97,6 +97,22 @@ int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int bat
                   hipStream_t stream);
 
 /*
+ * attn_quant_kv -- the Sage flow's two input passes in one launch: K int8 per
+ * 128-token block (exactly attn_quant_qk with INT8_PER_BLOCK on k) and V to
+ * the permuted V^T layout unchanged (exactly attn_quant_v_permute with mode
+ * NONE on v); the two run side by side in one grid instead of one after the
+ * other (PaddleNLP "Sage Attention Support Varlen": the varlen "quant qk" and
+ * "quant_transpose_permute v" steps).
+ *   k, v [total_tokens, num_kv_heads, head_dim] of `dtype` (BF16 or FP16).
+ *   k_codes int8 same shape; k_scales fp32 [batch, num_kv_heads,
+ *   ceil(max_seqlen/128)]; v_out [batch, num_kv_heads, head_dim,
+ *   round_up(max_seqlen, 128)] 16-bit.  block_tokens must be 128.
+ */
+int attn_quant_kv(const void* k, const void* v, int dtype, const int32_t* cu_seqlens, int batch,
+                  int max_seqlen, int total_tokens, int num_kv_heads, int head_dim, int block_tokens,
+                  void* k_codes, float* k_scales, void* v_out, hipStream_t stream);
+
+/*
  * attn_quant_v_permute -- the varlen "quant_transpose_permute v" step
  * (PaddleNLP "Sage Attention Support Varlen").
  *   v      [total_tokens, num_kv_heads, head_dim], BF16 or FP16.

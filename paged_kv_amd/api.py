@@ -19,7 +19,7 @@ __all__ = [
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
     "attn_smooth_quant_k", "attn_gather_paged_kv", "attn_decode_paged_workspace_size",
     "attn_decode_paged",
-    "attn_sparse_mla_decode_workspace_size", "attn_sparse_mla_decode",
+    "attn_sparse_mla_decode_workspace_size", "attn_sparse_mla_decode", "attn_quant_kv",
     "SYMBOLS",
 ]
 
@@ -37,6 +37,7 @@ SYMBOLS = {
     "attnq_abi_version": (_I, []),
     "attnq_last_error": (ctypes.c_char_p, []),
     "attn_quant_qk": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "attn_quant_kv": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "attn_quant_v_permute": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "attn_append_kv_rope": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P,
                                  _P, _P, _I, _I, _P, _P, _P, _P]),
@@ -109,6 +110,14 @@ def attn_quant_qk(x, x_dtype, cu_seqlens, batch, max_seqlen, total_tokens, num_h
     _check(lib().attn_quant_qk(_ptr(x), x_dtype, _ptr(cu_seqlens), batch, max_seqlen, total_tokens,
                                num_heads, head_dim, mode, block_tokens, _ptr(amax_in), _ptr(codes),
                                _ptr(scales), s), "attn_quant_qk")
+
+
+def attn_quant_kv(k, v, dtype, cu_seqlens, batch, max_seqlen, total_tokens, num_kv_heads, head_dim,
+                  block_tokens, k_codes, k_scales, v_out, stream=None):
+    s = _stream(stream, k, v_out)
+    _check(lib().attn_quant_kv(_ptr(k), _ptr(v), dtype, _ptr(cu_seqlens), batch, max_seqlen, total_tokens,
+                               num_kv_heads, head_dim, block_tokens, _ptr(k_codes), _ptr(k_scales), _ptr(v_out),
+                               s), "attn_quant_kv")
 
 
 def attn_quant_v_permute(v, v_dtype, cu_seqlens, batch, max_seqlen, total_tokens, num_kv_heads,

@@ -106,6 +106,32 @@ int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int bat
   return ok();
 }
 
+// ---------------------------------------------------------------- attn_quant_kv
+int attn_quant_kv(const void* k, const void* v, int dtype, const int32_t* cu_seqlens, int batch,
+                  int max_seqlen, int total_tokens, int num_kv_heads, int head_dim, int block_tokens,
+                  void* k_codes, float* k_scales, void* v_out, hipStream_t stream) {
+  REQUIRE(is16(dtype), ATTNQ_EUNSUPPORTED, "dtype must be BF16 or FP16");
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_kv_heads > 0 && num_kv_heads <= 1024, ATTNQ_EINVAL, "num_kv_heads must be in [1, 1024]");
+  REQUIRE(block_tokens == 128, ATTNQ_EUNSUPPORTED, "block_tokens must be 128 (got %d)", block_tokens);
+  REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0, ATTNQ_EINVAL, "sizes must be >= 0");
+  REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
+  if (batch == 0 || max_seqlen == 0) return ok();
+  REQUIRE_PTR(cu_seqlens, 4);
+  REQUIRE_PTR(k_scales, 4);
+  REQUIRE_PTR(v_out, 16);
+  if (total_tokens > 0) {
+    REQUIRE_PTR(k, 16);
+    REQUIRE_PTR(v, 16);
+    REQUIRE_PTR(k_codes, 16);
+  }
+  const int nblk = (max_seqlen + 127) / 128;
+  LAUNCHED(attnq::launch_quant_k_permute_v(k, v, cu_seqlens, batch, num_kv_heads, head_dim, nblk,
+                                           round_up(max_seqlen, 128), dtype == ATTNQ_BF16, total_tokens,
+                                           k_codes, k_scales, v_out, stream));
+  return ok();
+}
+
 // ---------------------------------------------------------------- attn_quant_v_permute
 int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, int batch,
                          int max_seqlen, int total_tokens, int num_kv_heads, int head_dim,

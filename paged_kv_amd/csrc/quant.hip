@@ -120,14 +120,14 @@ constexpr int I8_BLOCK = 128;
 
 // SMOOTH: the values quantized are x - mean[b][h][channel] (fp32, rounded
 // once), the sequence's per-channel mean of K written by k_channel_mean.
-template <bool BF16, int DIM, bool SMOOTH = false>
-__global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int nblk,
-    int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales,
-    const float* __restrict__ mean = nullptr) {
+// The work of one workgroup (block j, head h, sequence b).
+template <bool BF16, int DIM, bool SMOOTH>
+__device__ __forceinline__ void quant_int8_block_wg(
+    int j, int h, int b, const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads,
+    int nblk, int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales,
+    const float* __restrict__ mean) {
   constexpr int CPR = DIM / 8;                          // 16-byte chunks per row
   constexpr int NCH = I8_BLOCK * CPR / I8_THREADS;      // chunks per thread
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
   const int r0 = s0 + j * I8_BLOCK;
   float* sc_out = scales + ((long)b * heads + h) * nblk + j;
@@ -194,6 +194,15 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
   };
   if (scale >= QUOT_MIN_SCALE) encode_all(std::true_type{});  // uniform
   else encode_all(std::false_type{});
+}
+
+template <bool BF16, int DIM, bool SMOOTH = false>
+__global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int nblk,
+    int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales,
+    const float* __restrict__ mean = nullptr) {
+  quant_int8_block_wg<BF16, DIM, SMOOTH>(blockIdx.x, blockIdx.y, blockIdx.z, x, cu, heads, nblk, total_tokens,
+                                         codes, scales, mean);
 }
 
 // ---------------------------------------------------------------- per-channel mean of K
@@ -306,12 +315,13 @@ __global__ __launch_bounds__(CA_THREADS) void k_channel_amax(
 constexpr int VP_THREADS = 256;
 constexpr int VP_TILE = 64;
 
-__global__ __launch_bounds__(VP_THREADS) void k_v_permute(
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu, int heads, int dim,
-    int s_pad, int is_bf16, int total_tokens, int fp8, int wide, const float* __restrict__ descale,
-    void* __restrict__ out, int chan = 0) {
+// The work of one workgroup (64-token tile, head h, sequence b).
+__device__ __forceinline__ void v_permute_wg(
+    int tile, int h, int b, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu, int heads,
+    int dim, int s_pad, int is_bf16, int total_tokens, int fp8, int wide, const float* __restrict__ descale,
+    void* __restrict__ out, int chan) {
   __shared__ uint16_t s_t[128][VP_TILE + 2];  // [d][token], padded rows
-  const int t0 = blockIdx.x * VP_TILE, h = blockIdx.y, b = blockIdx.z;
+  const int t0 = tile * VP_TILE;
   const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
   const int L = s1 - s0;
   const int cpr = dim / 8;
@@ -369,6 +379,33 @@ __global__ __launch_bounds__(VP_THREADS) void k_v_permute(
                      e16[6] | (e16[7] << 16));
     }
   }
+}
+
+__global__ __launch_bounds__(VP_THREADS) void k_v_permute(
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu, int heads, int dim,
+    int s_pad, int is_bf16, int total_tokens, int fp8, int wide, const float* __restrict__ descale,
+    void* __restrict__ out, int chan = 0) {
+  v_permute_wg(blockIdx.x, blockIdx.y, blockIdx.z, v, cu, heads, dim, s_pad, is_bf16, total_tokens, fp8, wide,
+               descale, out, chan);
+}
+
+// ---------------------------------------------------------------- K int8 blocks + V^T in one launch
+// The Sage flow's two input passes side by side: workgroups x < nblk quantize
+// K block x (as k_quant_int8_block), the others permute V tile x - nblk (as
+// k_v_permute with 16-bit V, no encoding).  Same outputs as the two launches.
+static_assert(I8_THREADS == VP_THREADS, "one workgroup size for both bodies");
+
+template <bool BF16, int DIM>
+__global__ __launch_bounds__(I8_THREADS) void k_quant_k_permute_v(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
+    int heads, int nblk, int s_pad, int total_tokens, int8_t* __restrict__ codes, float* __restrict__ scales,
+    void* __restrict__ v_out) {
+  if ((int)blockIdx.x < nblk)
+    quant_int8_block_wg<BF16, DIM, false>(blockIdx.x, blockIdx.y, blockIdx.z, k, cu, heads, nblk, total_tokens,
+                                          codes, scales, nullptr);
+  else
+    v_permute_wg(blockIdx.x - nblk, blockIdx.y, blockIdx.z, v, cu, heads, DIM, s_pad, BF16, total_tokens, 0, 0,
+                 nullptr, v_out, 0);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -460,6 +497,24 @@ bool launch_smooth_quant_int8_block(const void* x, const int32_t* cu, int batch,
   if (dim == 128) hipLaunchKernelGGL((k_quant_int8_block<false, 128, true>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales, mean);
   else hipLaunchKernelGGL((k_quant_int8_block<false, 64, true>), grid, dim3(I8_THREADS), 0, s, xp, cu, heads, nblk, total_tokens, cp, scales, mean);
   return hipGetLastError() == hipSuccess;
+}
+
+bool launch_quant_k_permute_v(const void* k, const void* v, const int32_t* cu, int batch, int heads, int dim,
+                              int nblk, int s_pad, bool is_bf16, int total_tokens, void* codes, float* scales,
+                              void* v_out, hipStream_t s) {
+  if (batch <= 0 || nblk <= 0) return true;
+  const dim3 grid(nblk + s_pad / VP_TILE, heads, batch);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  int8_t* cp = static_cast<int8_t*>(codes);
+  if (dim == 128) {
+    if (is_bf16) hipLaunchKernelGGL((k_quant_k_permute_v<true, 128>), grid, dim3(I8_THREADS), 0, s, kp, vp, cu, heads, nblk, s_pad, total_tokens, cp, scales, v_out);
+    else hipLaunchKernelGGL((k_quant_k_permute_v<false, 128>), grid, dim3(I8_THREADS), 0, s, kp, vp, cu, heads, nblk, s_pad, total_tokens, cp, scales, v_out);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((k_quant_k_permute_v<true, 64>), grid, dim3(I8_THREADS), 0, s, kp, vp, cu, heads, nblk, s_pad, total_tokens, cp, scales, v_out);
+    else hipLaunchKernelGGL((k_quant_k_permute_v<false, 64>), grid, dim3(I8_THREADS), 0, s, kp, vp, cu, heads, nblk, s_pad, total_tokens, cp, scales, v_out);
+  }
+  return ok(hipGetLastError());
 }
 
 bool launch_v_permute_per_channel(const void* v, const int32_t* cu, int batch, int heads, int dim,

@@ -1,5 +1,6 @@
-// Launch interface of the SageAttention refinements of the quantizers (quant.hip):
-// K smoothing before the int8 block quantization, fp8 V with per-channel descales.
+// Launch interface of the Sage-flow quantizers beyond launch.h (quant.hip): K
+// smoothing before the int8 block quantization, fp8 V with per-channel
+// descales, and K int8 blocks with the V permute in one launch.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,5 +19,11 @@ bool launch_smooth_quant_int8_block(const void* x, const int32_t* cu, int batch,
 bool launch_v_permute_per_channel(const void* v, const int32_t* cu, int batch, int heads, int dim,
                                   int s_pad, bool is_bf16, int total_tokens, bool wide,
                                   float* descale, void* out, hipStream_t s);
+
+// k int8 per 128-token block (codes, scales [batch, heads, nblk]) and v -> V^T
+// [batch, heads, dim, s_pad] unchanged 16-bit values, in one launch.
+bool launch_quant_k_permute_v(const void* k, const void* v, const int32_t* cu, int batch, int heads, int dim,
+                              int nblk, int s_pad, bool is_bf16, int total_tokens, void* codes, float* scales,
+                              void* v_out, hipStream_t s);
 
 }  // namespace attnq

@@ -123,6 +123,11 @@ class SagePrefill:
         if not self.fuse_q:
             A.attn_quant_qk(self.q, _dtype_code(self.q), self.cu, self.b, self.max_seqlen, self.t,
                             self.hq, self.d, A.Q_INT8_PER_BLOCK, 128, None, self.qc, self.qs)
+        if not self.smooth_k and not self.v_chan and self.k.dtype == self.v.dtype:
+            # K int8 blocks and the V permute side by side in one launch
+            A.attn_quant_kv(self.k, self.v, _dtype_code(self.k), self.cu, self.b, self.max_seqlen, self.t,
+                            self.hkv, self.d, 128, self.kc, self.ks, self.vp)
+            return
         if self.smooth_k:
             A.attn_smooth_quant_k(self.k, self.cu, self.b, self.max_seqlen, self.t, self.hkv, self.d, 128,
                                   self.kc, self.ks, self.kmean)

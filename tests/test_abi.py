@@ -23,7 +23,7 @@ def _declared():
 
 def test_header_declares_the_calls():
     names = set(_declared())
-    for n in ["attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
+    for n in ["attn_quant_qk", "attn_quant_kv", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
               "attn_gather_paged_kv", "attn_decode_paged", "attn_sparse_mla_decode"]:
         assert n in names
 
@@ -202,3 +202,20 @@ def test_python_binding_raises_with_message():
     with pytest.raises(RuntimeError, match="head_dim"):
         pk.attn_quant_qk(FAKE, pk.BF16, FAKE, 1, 10, 10, 2, 96, pk.Q_FP8_PER_HEAD, 128, None, FAKE,
                          FAKE, stream=0)
+
+
+def _qkv(**kw):
+    a = dict(k=FAKE, v=FAKE, dt=pk.FP16, cu=FAKE, b=2, mx=300, t=400, h=8, d=128, bt=128, kc=FAKE, ks=FAKE, vo=FAKE,
+             st=None)
+    a.update(kw)
+    return pk.lib().attn_quant_kv(*a.values())
+
+
+def test_quant_kv_validation():
+    assert _qkv(dt=pk.INT8) == -2 and "dtype" in _err()
+    assert _qkv(d=96) == -2 and "head_dim" in _err()
+    assert _qkv(bt=64) == -2 and "block_tokens" in _err()
+    assert _qkv(h=0) == -1
+    assert _qkv(vo=None) == -1 and "v_out" in _err()
+    assert _qkv(kc=FAKE + 8) == -1 and "aligned" in _err()
+    assert _qkv(b=0, k=None, v=None, cu=None) == 0           # nothing to do
