@@ -27,6 +27,8 @@
  *    from device memory to the buffer bounds given on the host, so a broken
  *    precondition gives wrong values, never an out-of-bounds access.
  *  - Pointers must be 16-byte aligned (4-byte for int32/fp32 arrays).
+ *  - batch (batch * s_q for the sparse MLA decode) is at most 65535, a
+ *    grid dimension of the launches; larger values give ATTNQ_EUNSUPPORTED.
  *  - Layouts are row-major, last index contiguous.  T = total tokens of a
  *    varlen batch; cu_seqlens are int32 prefix sums [B+1], cu[0] = 0,
  *    cu[B] = T (the FlashInfer qo_indptr / kv_indptr of a ragged batch).

@@ -97,6 +97,7 @@ int attn_quant_qk(const void* x, int x_dtype, const int32_t* cu_seqlens, int bat
   }
   REQUIRE(block_tokens == 128, ATTNQ_EUNSUPPORTED, "block_tokens must be 128 (got %d)", block_tokens);
   REQUIRE(batch >= 0, ATTNQ_EINVAL, "batch must be >= 0");
+  REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
   REQUIRE(max_seqlen >= 0, ATTNQ_EINVAL, "max_seqlen must be >= 0");
   REQUIRE(amax_in == nullptr, ATTNQ_EINVAL, "amax_in applies to FP8_PER_HEAD only");
   REQUIRE_PTR(cu_seqlens, 4);
@@ -141,6 +142,7 @@ int attn_quant_v_permute(const void* v, int v_dtype, const int32_t* cu_seqlens, 
   REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   REQUIRE(num_kv_heads > 0 && num_kv_heads <= 1024, ATTNQ_EINVAL, "num_kv_heads must be in [1, 1024]");
   REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0, ATTNQ_EINVAL, "sizes must be >= 0");
+  REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
   const bool chan = mode == ATTNQ_Q_FP8_PER_CHANNEL || mode == ATTNQ_Q_FP8_PER_CHANNEL_WIDE;
   REQUIRE(mode == ATTNQ_Q_FP8_PER_HEAD || mode == ATTNQ_Q_FP8_PER_HEAD_WIDE || mode == ATTNQ_Q_NONE || chan,
           ATTNQ_EINVAL, "mode must be FP8_PER_HEAD, FP8_PER_HEAD_WIDE, FP8_PER_CHANNEL, FP8_PER_CHANNEL_WIDE or NONE");
@@ -301,7 +303,7 @@ int attn_smooth_quant_k(const void* k, const int32_t* cu_seqlens, int batch, int
   REQUIRE(block_tokens == 128, ATTNQ_EUNSUPPORTED, "block_tokens must be 128 (got %d)", block_tokens);
   REQUIRE(batch >= 0 && max_seqlen >= 0 && total_tokens >= 0 && num_kv_heads > 0, ATTNQ_EINVAL,
           "batch, max_seqlen, total_tokens must be >= 0 and num_kv_heads > 0");
-  REQUIRE(num_kv_heads <= 65535, ATTNQ_EUNSUPPORTED, "num_kv_heads too large");
+  REQUIRE(num_kv_heads <= 65535 && batch <= 65535, ATTNQ_EUNSUPPORTED, "num_kv_heads and batch must be <= 65535");
   if (batch == 0) return ok();
   REQUIRE_PTR(cu_seqlens, 4);
   REQUIRE_PTR(mean, 4);
@@ -329,6 +331,7 @@ int attn_gather_paged_kv(const void* cache, int elem_bytes, const int32_t* kv_in
   REQUIRE(num_kv_heads > 0 && num_pages > 0 && page_size > 0, ATTNQ_EINVAL,
           "num_kv_heads, num_pages and page_size must be positive");
   REQUIRE(batch >= 0 && max_seqlen_k >= 0, ATTNQ_EINVAL, "batch and max_seqlen_k must be >= 0");
+  REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
   if (batch == 0 || max_seqlen_k == 0) return ok();
   REQUIRE((long)num_kv_heads * head_dim * elem_bytes < (1L << 20), ATTNQ_EUNSUPPORTED, "row too wide");
   REQUIRE_PTR(cache, 16);
@@ -368,6 +371,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   REQUIRE(page_size >= 16 && page_size <= 1024 && page_size % 16 == 0, ATTNQ_EINVAL,
           "page_size must be a multiple of 16 in [16, 1024] (got %d)", page_size);
   REQUIRE(batch >= 0 && max_kv_len >= 0, ATTNQ_EINVAL, "batch and max_kv_len must be >= 0");
+  REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
   REQUIRE(num_pages > 0, ATTNQ_EINVAL, "num_pages must be positive");
   REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
   if (batch == 0) return ok();
@@ -435,6 +439,7 @@ int attn_sparse_mla_decode(const void* q, const void* kv_cache, int kv_dtype, co
   REQUIRE(block_size >= 16 && block_size <= 1024 && block_size % 16 == 0, ATTNQ_EINVAL,
           "block_size must be a multiple of 16 in [16, 1024] (got %d)", block_size);
   REQUIRE(batch >= 0 && s_q >= 0, ATTNQ_EINVAL, "batch and s_q must be >= 0");
+  REQUIRE((long)batch * s_q <= 65535, ATTNQ_EUNSUPPORTED, "batch * s_q must be <= 65535");
   REQUIRE(num_blocks > 0 && max_blocks_per_seq > 0, ATTNQ_EINVAL, "num_blocks and max_blocks_per_seq must be positive");
   REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
   if (batch == 0 || s_q == 0) return ok();

@@ -219,3 +219,14 @@ def test_quant_kv_validation():
     assert _qkv(vo=None) == -1 and "v_out" in _err()
     assert _qkv(kc=FAKE + 8) == -1 and "aligned" in _err()
     assert _qkv(b=0, k=None, v=None, cu=None) == 0           # nothing to do
+
+
+def test_grid_dimension_limits():
+    L = pk.lib()
+    assert _smooth(b=70000) == -2 and "batch" in _err()
+    assert _mla(b=300, sq=300) == -2 and "s_q" in _err()
+    assert _qkv(b=70000) == -2 and "batch" in _err()
+    assert _gather(b=70000) == -2 and "batch" in _err()
+    assert L.attn_quant_v_permute(FAKE, pk.BF16, FAKE, 70000, 10, 10, 2, 64, pk.Q_NONE, None, FAKE, None, None) == -2
+    assert L.attn_quant_qk(FAKE, pk.BF16, FAKE, 70000, 10, 10, 2, 64, pk.Q_INT8_PER_BLOCK, 128, None, FAKE, FAKE,
+                           None) == -2
