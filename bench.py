@@ -282,12 +282,15 @@ def bench_paged_prefill(iters, cpu=False):
     settle(p.attend)
     kms = time_events(p.attend, iters)
     pipe = time_events(p.run, max(2, iters // 2))
+    gms = float(np.median(time_events(p.gather, iters)))
     med = float(np.median(kms))
     r = {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
          "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
          "pipeline_ms": float(np.median(pipe)),
          "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12,
-         "gathered_bytes": float(2 * np.sum(lk) * 8 * 128 * 2)}
+         "gathered_bytes": float(2 * np.sum(lk) * 8 * 128 * 2),
+         # the page gather alone: every cached K and V row read once and written once
+         "gather_ms": gms, "gather_GB/s": 2 * float(2 * np.sum(lk) * 8 * 128 * 2) / (gms * 1e-3) / 1e9}
     if cpu:
         r["cpu_oracle"] = oracle_paged_prefill(x)
     return r
