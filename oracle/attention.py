@@ -24,8 +24,13 @@ Functions:
   decode_paged       FlashInfer's batch decode over a paged KV cache
                      (indptr / indices / last_page_len), fp8 K/V with
                      per-head descales (aiter's paged fp8 flash_attn_with_kvcache)
-  sparse_mla_decode  the Ascend operator: MLA-absorb, 656-byte combined rows,
-                     per-token tile-128 scales, block_table, sparse_indices
+  sparse_mla_decode  the Ascend operator: MLA-absorb, 656-byte combined rows
+                     (int8 or fp8 e4m3 nope codes), per-token tile-128 scales,
+                     block_table, sparse_indices, sparse_block_size, sparse_mode
+                     0 or 3; sparse_mla_tokens states which tokens a query
+                     row uses
+  ragged_from_pages  a paged cache read back into the ragged [T, H, D] layout
+  dequant_*          code * scale for fp8 per head / per channel and int8 per block
   lse_merge          combination of split partials (O_c, lse_c)
 
 Pins (tests/test_oracle_attention.py): pure-Python brute force
@@ -33,7 +38,10 @@ Pins (tests/test_oracle_attention.py): pure-Python brute force
 gives that V row; constant V gives V; scale 0 gives the mean of the visible
 V rows and lse = ln(n); V = 1 gives 1 (rows of P sum to 1); garbage in the
 masked tail has no effect; the two-key closed form; split + merge equals
-no split; page permutation invariance; sparse over all tokens equals dense.
+no split; page permutation invariance; sparse over all tokens equals dense;
+block-sparse equals its token expansion; the right-down causal mode equals
+mode 0 on the filtered indices; a page walk and the append round trip for
+ragged_from_pages; K smoothing leaves the softmax output unchanged.
 """
 from __future__ import annotations
 
