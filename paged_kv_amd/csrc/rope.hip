@@ -14,7 +14,7 @@
 namespace attnq {
 
 constexpr int RP_THREADS = 256;
-constexpr int RP_TOKENS = 16;      // tokens per workgroup
+constexpr int RP_TOKENS = 2;       // tokens per workgroup (each walks its tokens one after another)
 constexpr int RP_MAXK = 32;        // units per thread per token (<= 8192 units)
 constexpr int RP_MAX_HEADS = 1024;
 constexpr int RP_MAX_CU = 1024;    // cu_seqlens cached in LDS up to this many entries
