@@ -25,6 +25,62 @@ __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
 constexpr int AMAX_THREADS = 256;
 constexpr int AMAX_ROWS_PER_BLOCK = 64;
 
+// Rows of at most AMAX_THREADS * 8 chunks: every thread keeps fixed columns
+// (so fixed heads) for all rows of the block -- NCOL columns c = t + 256k of
+// each row, or, for rows narrower than the workgroup, column t % cpr of rows
+// t / cpr, t / cpr + 256 / cpr, ... -- with one running max per column, the
+// loads of 4 rows in flight at once, and one LDS atomic per column at the end.
+template <int NCOL>
+__global__ __launch_bounds__(AMAX_THREADS) void k_amax_per_head_cols(
+    const uint16_t* __restrict__ x, int rows, int heads, int dim, int is_bf16,
+    uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t s_max[1024];
+  for (int i = threadIdx.x; i < heads; i += AMAX_THREADS) s_max[i] = 0u;
+  __syncthreads();
+  const int cpr = heads * dim / 8;  // 16-byte chunks per row
+  const int row0 = blockIdx.x * AMAX_ROWS_PER_BLOCK;
+  const int nrows = min(AMAX_ROWS_PER_BLOCK, rows - row0);
+  const uint4* src = reinterpret_cast<const uint4*>(x) + (long)row0 * cpr;
+  const int rstep = cpr >= AMAX_THREADS ? 1 : AMAX_THREADS / cpr;   // rows per pass
+  const int rfirst = cpr >= AMAX_THREADS ? 0 : threadIdx.x / cpr;
+  const int col0 = cpr >= AMAX_THREADS ? threadIdx.x : threadIdx.x % cpr;
+  const bool live = rfirst < rstep;   // threads past the last whole row of a pass idle
+  float m[NCOL];
+#pragma unroll
+  for (int k = 0; k < NCOL; ++k) m[k] = 0.0f;
+  for (int r = rfirst; live && r < nrows; r += 4 * rstep) {
+    uint4 v[4][NCOL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < NCOL; ++k) {
+        const int rr = r + u * rstep, c = col0 + k * AMAX_THREADS;
+        v[u][k] = rr < nrows && c < cpr ? src[(long)rr * cpr + c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < NCOL; ++k) {
+        const uint32_t w[4] = {v[u][k].x, v[u][k].y, v[u][k].z, v[u][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m[k] = fmaxf(m[k], fabsf(h16_to_f32(w[e] & 0xffffu, is_bf16)));
+          m[k] = fmaxf(m[k], fabsf(h16_to_f32(w[e] >> 16, is_bf16)));
+        }
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < NCOL; ++k) {
+    const int c = col0 + k * AMAX_THREADS;
+    if (live && c < cpr && m[k] != 0.0f) atomicMax(&s_max[c * 8 / dim], __float_as_uint(m[k]));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < heads; i += AMAX_THREADS)
+    if (s_max[i]) atomicMax(&amax_bits[i], s_max[i]);
+}
+
+// Any row width: a thread walks the block's chunks with a stride of the
+// workgroup size, folding its max into LDS whenever the head changes.
 __global__ __launch_bounds__(AMAX_THREADS) void k_amax_per_head(
     const uint16_t* __restrict__ x, int rows, int heads, int dim, int is_bf16,
     uint32_t* __restrict__ amax_bits) {
@@ -74,7 +130,7 @@ __global__ void k_finalize_scale(const float* __restrict__ amax_in, float* scale
 // reciprocal) for FP8_ROWS consecutive rows, whose loads are all in flight
 // before the first is encoded.
 constexpr int FP8_THREADS = 256;
-constexpr int FP8_ROWS = 16;
+constexpr int FP8_ROWS = 8;   // measured: 8 beats 16 (-6%) and 32
 
 template <bool BF16, int CPRH>
 __global__ __launch_bounds__(FP8_THREADS) void k_quant_fp8(const uint16_t* __restrict__ x, int rows, int heads,
@@ -421,8 +477,13 @@ bool launch_amax(const void* x, int rows, int heads, int dim, bool is_bf16, uint
                  hipStream_t s) {
   if (rows <= 0) return true;
   int grid = (rows + AMAX_ROWS_PER_BLOCK - 1) / AMAX_ROWS_PER_BLOCK;
-  hipLaunchKernelGGL(k_amax_per_head, dim3(grid), dim3(AMAX_THREADS), 0, s,
-                     static_cast<const uint16_t*>(x), rows, heads, dim, (int)is_bf16, amax_bits);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const int ncol = (heads * dim / 8 + AMAX_THREADS - 1) / AMAX_THREADS;
+  if (ncol <= 1) hipLaunchKernelGGL(k_amax_per_head_cols<1>, dim3(grid), dim3(AMAX_THREADS), 0, s, xp, rows, heads, dim, (int)is_bf16, amax_bits);
+  else if (ncol <= 2) hipLaunchKernelGGL(k_amax_per_head_cols<2>, dim3(grid), dim3(AMAX_THREADS), 0, s, xp, rows, heads, dim, (int)is_bf16, amax_bits);
+  else if (ncol <= 4) hipLaunchKernelGGL(k_amax_per_head_cols<4>, dim3(grid), dim3(AMAX_THREADS), 0, s, xp, rows, heads, dim, (int)is_bf16, amax_bits);
+  else if (ncol <= 8) hipLaunchKernelGGL(k_amax_per_head_cols<8>, dim3(grid), dim3(AMAX_THREADS), 0, s, xp, rows, heads, dim, (int)is_bf16, amax_bits);
+  else hipLaunchKernelGGL(k_amax_per_head, dim3(grid), dim3(AMAX_THREADS), 0, s, xp, rows, heads, dim, (int)is_bf16, amax_bits);
   return ok(hipGetLastError());
 }
 
