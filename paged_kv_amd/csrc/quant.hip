@@ -267,20 +267,23 @@ __global__ __launch_bounds__(I8_THREADS) void k_quant_int8_block(
 // 0 for an empty sequence.  Every fp16 value is an integer number of 2^-24
 // units below 2^40, so a thread's fp64 partial sum of at most MEAN_FLUSH of
 // them stays below 2^53 units and is exact; partials are then added as int64
-// (order-free).  One workgroup per (head, sequence); thread (row group,
-// 16-byte channel chunk); finite inputs.
+// (order-free).  MEAN_SPLIT workgroups per (head, sequence), each owning a
+// contiguous share of the channels; thread (row group, 16-byte channel
+// chunk); finite inputs.
 constexpr int MEAN_THREADS = 1024;
 constexpr int MEAN_FLUSH = 8192;  // a multiple of MEAN_BATCH
 constexpr int MEAN_BATCH = 8;
+constexpr int MEAN_SPLIT = 2;     // workgroups per (head, sequence), by channel
 
 template <int DIM>
 __global__ __launch_bounds__(MEAN_THREADS) void k_channel_mean(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int heads, int total_tokens,
     float* __restrict__ mean) {
-  constexpr int CPR = DIM / 8, G = MEAN_THREADS / CPR;  // chunks per row, row groups
+  constexpr int CPR = DIM / 8 / MEAN_SPLIT, G = MEAN_THREADS / CPR;  // this workgroup's chunks per row, row groups
+  static_assert(CPR >= 1 && 64 % CPR == 0, "a wave holds whole rows of chunk columns");
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = threadIdx.x % CPR, g = threadIdx.x / CPR;
+  const int col = blockIdx.z * CPR + threadIdx.x % CPR, g = threadIdx.x / CPR;
   const int s0 = clampi(cu[b], 0, total_tokens), s1 = clampi(cu[b + 1], s0, total_tokens);
   long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (long c0 = s0 + g; c0 < s1; c0 += (long)G * MEAN_FLUSH) {
@@ -314,7 +317,8 @@ __global__ __launch_bounds__(MEAN_THREADS) void k_channel_mean(
     for (int e = 0; e < 8; ++e) s_acc[wave][col * 8 + e] = acc[e];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < DIM; c += MEAN_THREADS) {
+  for (int c = blockIdx.z * (DIM / MEAN_SPLIT) + threadIdx.x; c < (blockIdx.z + 1) * (DIM / MEAN_SPLIT);
+       c += MEAN_THREADS) {
     long long tot = 0;
     for (int w = 0; w < MEAN_THREADS / 64; ++w) tot += s_acc[w][c];
     const int L = s1 - s0;
@@ -550,8 +554,8 @@ bool launch_smooth_quant_int8_block(const void* x, const int32_t* cu, int batch,
   if (batch <= 0) return true;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   int8_t* cp = static_cast<int8_t*>(codes);
-  if (dim == 128) hipLaunchKernelGGL((k_channel_mean<128>), dim3(heads, batch), dim3(MEAN_THREADS), 0, s, xp, cu, heads, total_tokens, mean);
-  else hipLaunchKernelGGL((k_channel_mean<64>), dim3(heads, batch), dim3(MEAN_THREADS), 0, s, xp, cu, heads, total_tokens, mean);
+  if (dim == 128) hipLaunchKernelGGL((k_channel_mean<128>), dim3(heads, batch, MEAN_SPLIT), dim3(MEAN_THREADS), 0, s, xp, cu, heads, total_tokens, mean);
+  else hipLaunchKernelGGL((k_channel_mean<64>), dim3(heads, batch, MEAN_SPLIT), dim3(MEAN_THREADS), 0, s, xp, cu, heads, total_tokens, mean);
   if (hipGetLastError() != hipSuccess) return false;
   if (nblk <= 0) return true;
   const dim3 grid(nblk, heads, batch);
