@@ -29,6 +29,10 @@
  *  - Pointers must be 16-byte aligned (4-byte for int32/fp32 arrays).
  *  - batch (batch * s_q for the sparse MLA decode) is at most 65535, a
  *    grid dimension of the launches; larger values give ATTNQ_EUNSUPPORTED.
+ *  - sm_scale (attention calls) is any finite value, zero and negative
+ *    values included, or NaN for the default 1/sqrt(d_k) (aiter's
+ *    softmax_scale=None; the Ascend scale_value): d_k = head_dim, and 576
+ *    for the sparse MLA decode.  Infinities give ATTNQ_EINVAL.
  *  - Layouts are row-major, last index contiguous.  T = total tokens of a
  *    varlen batch; cu_seqlens are int32 prefix sums [B+1], cu[0] = 0,
  *    cu[B] = T (the FlashInfer qo_indptr / kv_indptr of a ragged batch).
@@ -67,8 +71,11 @@ typedef enum {
                                        INT8_PER_BLOCK, int8 per-block K */
   ATTNQ_Q_FP8_PER_CHANNEL = 5,      /* V only: e4m3fn codes, one fp32 descale per (sequence, kv head,
                                        channel) */
-  ATTNQ_Q_FP8_PER_CHANNEL_WIDE = 6  /* V only: the codes of FP8_PER_CHANNEL stored as their exact
+  ATTNQ_Q_FP8_PER_CHANNEL_WIDE = 6, /* V only: the codes of FP8_PER_CHANNEL stored as their exact
                                        fp16 values */
+  ATTNQ_Q_FP8_PER_HEAD_MFMA8 = 7    /* attn_prefill_varlen only: FP8_PER_HEAD Q/K with QK^T on the
+                                       fp8 matrix instruction, whose 128-product sums carry a
+                                       relative error up to ~2^-11.8 of sum |q_d k_d| */
 } attnq_qmode;
 
 int attnq_abi_version(void);
@@ -176,7 +183,12 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  * (FlashInfer BatchPrefillWithRaggedKVCacheRun; aiter flash_attn_func with fp8
  * q/k/v and descales; PaddleNLP Sage attention over a varlen batch).
  *   q [total_q, num_q_heads, head_dim] and k [total_k, num_kv_heads, head_dim]:
- *     qk_dtype FP8E4M3 with scale_mode FP8_PER_HEAD (q_scale [Hq], k_scale [Hkv]), or
+ *     qk_dtype FP8E4M3 with scale_mode FP8_PER_HEAD (q_scale [Hq], k_scale [Hkv]): QK^T
+ *     is summed exactly (up to fp32 accumulation) from the codes' fp16 values; or
+ *     FP8E4M3 with FP8_PER_HEAD_MFMA8: the same scales, QK^T on the fp8 matrix
+ *     instruction (faster; each 128-term dot product may be off by ~2^-11.8 of
+ *     sum_d |q_d k_d|, which moves large logits -- outlier-heavy rows -- by more
+ *     than the output tolerance allows), or
  *     qk_dtype INT8 with scale_mode INT8_PER_BLOCK (q_scale [B, Hq, ceil(max_seqlen_q/128)],
  *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk), or
  *     qk_dtype BF16 / FP16 with scale_mode INT8_PER_BLOCK_RAW_Q: q is the unquantized
@@ -197,7 +209,9 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  *     writes zeros there): it meets p = 0 in the PV product.
  *   logit(i, j) = sm_scale * Dequant(q_i) . Dequant(k_j); q head h reads kv head
  *   h / (Hq/Hkv).  causal: key j visible to query i iff j <= i + L_k - L_q
- *   (bottom-right aligned).
+ *   (bottom-right aligned); a masked key contributes nothing whatever the
+ *   sign of sm_scale or of the scales.  With cu_seqlens_q != cu_seqlens_k a
+ *   sequence may have queries and no keys (its rows get o = 0, lse = -inf).
  *   o [total_q, num_q_heads, head_dim], o_dtype BF16 or FP16.
  *   lse optional fp32 [num_q_heads, total_q], natural log; rows with no visible
  *   key get o = 0 and lse = -inf.
@@ -272,7 +286,7 @@ int attn_gather_paged_kv(const void* cache, int elem_bytes, const int32_t* kv_in
  *   workspace: caller-owned device scratch of at least
  *   attn_decode_paged_workspace_size(...) bytes (partial O and lse).
  *   o bf16 [batch, num_q_heads, head_dim]; lse optional fp32 [batch, num_q_heads].
- *   Supported: head_dim 128, num_q_heads % num_kv_heads == 0, group <= 16,
+ *   Supported: head_dim 64 or 128, num_q_heads % num_kv_heads == 0, group <= 16,
  *   page_size a multiple of 16 and <= 1024.
  */
 size_t attn_decode_paged_workspace_size(int batch, int num_q_heads, int head_dim, int max_kv_len,
@@ -306,6 +320,9 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *   sparse_block_size in {1, 2, 4, 8, 16} (so it divides block_size).
  *   o bf16 [batch, s_q, num_heads, 512]; lse optional fp32 [batch, s_q, num_heads];
  *   rows with no used token get o = 0 and lse = -inf.
+ *   Tile scales: any value with |s| <= 2^100 (zero and negative included);
+ *   the kernels round p * s to bf16 with p <= 2^14, which stays finite in
+ *   that range.
  *   num_heads in {1,2,4,8,16,32,48,64,128}; block_size a multiple of 16, <= 1024;
  *   topk > 0.  workspace >= attn_sparse_mla_decode_workspace_size(...) bytes,
  *   256-byte aligned (0 is returned for invalid sizes).

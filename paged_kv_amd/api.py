@@ -14,6 +14,7 @@ import os
 
 __all__ = [
     "BF16", "FP16", "FP8E4M3", "INT8", "Q_FP8_PER_HEAD", "Q_INT8_PER_BLOCK", "Q_NONE", "Q_FP8_PER_HEAD_WIDE", "Q_FP8_PER_CHANNEL", "Q_FP8_PER_CHANNEL_WIDE",
+    "Q_FP8_PER_HEAD_MFMA8",
     "Q_INT8_PER_BLOCK_RAW_Q",
     "library_path", "lib", "abi_version",
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
@@ -25,7 +26,7 @@ __all__ = [
 
 BF16, FP16, FP8E4M3, INT8 = 0, 1, 2, 3
 Q_FP8_PER_HEAD, Q_INT8_PER_BLOCK, Q_NONE, Q_FP8_PER_HEAD_WIDE, Q_INT8_PER_BLOCK_RAW_Q = 0, 1, 2, 3, 4
-Q_FP8_PER_CHANNEL, Q_FP8_PER_CHANNEL_WIDE = 5, 6
+Q_FP8_PER_CHANNEL, Q_FP8_PER_CHANNEL_WIDE, Q_FP8_PER_HEAD_MFMA8 = 5, 6, 7
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

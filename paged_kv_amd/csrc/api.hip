@@ -57,6 +57,11 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 const float LOG2E = 1.4426950408889634f;
 
 bool is16(int dt) { return dt == ATTNQ_BF16 || dt == ATTNQ_FP16; }
+
+// sm_scale: any finite value, or NaN for the default 1/sqrt(d_k) (aiter's
+// softmax_scale=None; the Ascend scale_value); infinities are rejected.
+bool scale_ok(float s) { return std::isfinite(s) || std::isnan(s); }
+float scale_or_default(float s, int d_k) { return std::isnan(s) ? (float)(1.0 / std::sqrt((double)d_k)) : s; }
 int round_up(int x, int m) { return ((x + m - 1) / m) * m; }
 
 }  // namespace
@@ -231,12 +236,13 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0, ATTNQ_EINVAL,
           "num_q_heads must be a positive multiple of num_kv_heads");
-  const bool fp8qk = qk_dtype == ATTNQ_FP8E4M3 && scale_mode == ATTNQ_Q_FP8_PER_HEAD;
+  const bool fp8_mma8 = qk_dtype == ATTNQ_FP8E4M3 && scale_mode == ATTNQ_Q_FP8_PER_HEAD_MFMA8;
+  const bool fp8qk = (qk_dtype == ATTNQ_FP8E4M3 && scale_mode == ATTNQ_Q_FP8_PER_HEAD) || fp8_mma8;
   const bool i8qk = qk_dtype == ATTNQ_INT8 && scale_mode == ATTNQ_Q_INT8_PER_BLOCK;
   const bool rawq = is16(qk_dtype) && scale_mode == ATTNQ_Q_INT8_PER_BLOCK_RAW_Q;
   REQUIRE(fp8qk || i8qk || rawq, ATTNQ_EUNSUPPORTED,
-          "supported Q/K: FP8E4M3 with FP8_PER_HEAD scales, INT8 with INT8_PER_BLOCK scales, "
-          "or BF16/FP16 Q with INT8_PER_BLOCK_RAW_Q");
+          "supported Q/K: FP8E4M3 with FP8_PER_HEAD or FP8_PER_HEAD_MFMA8 scales, INT8 with "
+          "INT8_PER_BLOCK scales, or BF16/FP16 Q with INT8_PER_BLOCK_RAW_Q");
   REQUIRE(!rawq || (long)num_q_heads * head_dim < (1L << 22), ATTNQ_EUNSUPPORTED,
           "INT8_PER_BLOCK_RAW_Q: num_q_heads * head_dim must stay below 2^22");
   REQUIRE(v_dtype == ATTNQ_FP8E4M3 || v_dtype == ATTNQ_FP16, ATTNQ_EUNSUPPORTED, "v_dtype must be FP8E4M3 or FP16");
@@ -249,7 +255,8 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   REQUIRE((long)max_seqlen_k * num_kv_heads * head_dim < (1L << 31) &&
               (long)round_up(max_seqlen_k, 128) * head_dim * 2 < (1L << 31),
           ATTNQ_EUNSUPPORTED, "one sequence's K (max_seqlen_k * num_kv_heads * head_dim bytes) must stay below 2 GiB");
-  REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
+  REQUIRE(scale_ok(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite (or NaN for 1/sqrt(head_dim))");
+  sm_scale = scale_or_default(sm_scale, head_dim);
   REQUIRE_PTR(cu_seqlens_q, 4);
   REQUIRE_PTR(cu_seqlens_k, 4);
   if (rawq) REQUIRE_OPT_PTR(q_scale, 4);  // an output in this mode
@@ -287,7 +294,8 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   a.max_k = max_seqlen_k;
   a.sm_scale_log2 = sm_scale * LOG2E;
   if (total_q == 0) return ok();
-  const int q_mode = fp8qk ? attnq::PF_Q_FP8
+  const int q_mode = fp8_mma8 ? attnq::PF_Q_FP8_MFMA8
+                   : fp8qk ? attnq::PF_Q_FP8
                    : i8qk  ? attnq::PF_Q_I8
                    : qk_dtype == ATTNQ_BF16 ? attnq::PF_Q_RAW_BF16 : attnq::PF_Q_RAW_F16;
   LAUNCHED(attnq::launch_prefill(a, head_dim, q_mode, v_dtype == ATTNQ_FP8E4M3, o_dtype == ATTNQ_BF16,
@@ -364,7 +372,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int num_pages, int page_size, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_kv_len, float sm_scale, void* workspace,
                       size_t workspace_bytes, void* o, float* lse, hipStream_t stream) {
-  REQUIRE(head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0, ATTNQ_EINVAL,
           "num_q_heads must be a positive multiple of num_kv_heads");
   REQUIRE(num_q_heads / num_kv_heads <= 16, ATTNQ_EUNSUPPORTED, "at most 16 q heads per kv head");
@@ -373,7 +381,8 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   REQUIRE(batch >= 0 && max_kv_len >= 0, ATTNQ_EINVAL, "batch and max_kv_len must be >= 0");
   REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
   REQUIRE(num_pages > 0, ATTNQ_EINVAL, "num_pages must be positive");
-  REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
+  REQUIRE(scale_ok(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite (or NaN for 1/sqrt(head_dim))");
+  sm_scale = scale_or_default(sm_scale, head_dim);
   if (batch == 0) return ok();
   REQUIRE_PTR(q, 16);
   REQUIRE_PTR(k_cache, 16);
@@ -404,7 +413,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = a.ws_o + rows * head_dim;
   a.sm_scale_log2 = sm_scale * LOG2E;
-  LAUNCHED(attnq::launch_decode(a, stream));
+  LAUNCHED(attnq::launch_decode(a, head_dim, stream));
   return ok();
 }
 
@@ -441,7 +450,8 @@ int attn_sparse_mla_decode(const void* q, const void* kv_cache, int kv_dtype, co
   REQUIRE(batch >= 0 && s_q >= 0, ATTNQ_EINVAL, "batch and s_q must be >= 0");
   REQUIRE((long)batch * s_q <= 65535, ATTNQ_EUNSUPPORTED, "batch * s_q must be <= 65535");
   REQUIRE(num_blocks > 0 && max_blocks_per_seq > 0, ATTNQ_EINVAL, "num_blocks and max_blocks_per_seq must be positive");
-  REQUIRE(std::isfinite(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite");
+  REQUIRE(scale_ok(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite (or NaN for 1/sqrt(576))");
+  sm_scale = scale_or_default(sm_scale, 576);  // d_k of K = [nope 512 | rope 64]
   if (batch == 0 || s_q == 0) return ok();
   REQUIRE_PTR(q, 16);
   REQUIRE_PTR(kv_cache, 16);

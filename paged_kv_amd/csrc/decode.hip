@@ -32,20 +32,26 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* dec_lds_t;
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_D = 128;
 constexpr int DEC_CHUNK_TOKENS = 512;
 constexpr int DEC_BLKS = DEC_CHUNK_TOKENS / 16;    // 16-token blocks per chunk (one table lane each)
 static_assert(DEC_BLKS <= 64, "the block table lives in one VGPR");
 constexpr int DEC_STEP = 32;                      // tokens per step
 constexpr int DEC_VST = 2;                        // V stages per wave
-constexpr int DEC_VTILE = DEC_STEP * DEC_D;       // bytes of one fp8 V stage
 constexpr float DEC_LN2 = 0.69314718055994530942f;
 constexpr float DEC_REF_SLACK = 8.0f;             // log2 headroom before a rescale
 
-// 16-byte chunk position of chunk c in V tile row t (bank-conflict-free
-// transposed reads: the 8 rows one 16-lane group reads land in 8 distinct
-// (row parity, chunk) bank groups)
-ATTNQ_DEV int dec_vsw(int t) { return ((t >> 1) + 2 * (t >> 4)) & 7; }
+// 16-byte chunk position of chunk c in V tile row t is c ^ dec_vsw<D>(t), so
+// that the rows the transposed reads of one LDS pass name land in distinct
+// bank groups.  D = 128 (8 chunks per row): the 8 rows one 16-lane group
+// reads fall in 8 distinct (row parity, chunk) groups.  D = 64 (4 chunks,
+// rows 16 banks apart): the 16 rows two 16-lane groups read, 4g + r and
+// 16 + 4g + r for g in {0, 1} or {2, 3}, take the 4 row offsets times the 4
+// chunk positions.
+template <int D>
+ATTNQ_DEV int dec_vsw(int t) {
+  if constexpr (D == 128) return ((t >> 1) + 2 * (t >> 4)) & 7;
+  else return ((t >> 2) & 1) | (((t >> 4) & 1) << 1);
+}
 
 template <int N>
 ATTNQ_DEV void dec_wait_vm() {
@@ -53,7 +59,14 @@ ATTNQ_DEV void dec_wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt[3:0]; expcnt, lgkmcnt: no wait
 }
 
+template <int D>
 __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArgs a) {
+  constexpr int DEC_VTILE = DEC_STEP * D;           // bytes of one fp8 V stage
+  constexpr int NM = D / 32;                        // QK MFMAs per 16-token block
+  constexpr int KH = D / 64;                        // 64-byte halves of a K row
+  constexpr int RPL = 1024 / D;                     // V rows per 1 KB direct load
+  constexpr int CPR = D / 16;                       // 16-byte chunks per V row
+  constexpr int NVL = DEC_STEP * D / 1024;          // V direct loads per step
   __shared__ __attribute__((aligned(16))) uint8_t s_v[4][DEC_VST][DEC_VTILE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -72,7 +85,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
   const int vb_last = t_end - (t_begin + 16 * (nblk - 1));  // valid tokens of the last block
   const int nsteps = (nblk + 1) / 2;
   const int G = a.hq / a.hkv;
-  const long row_bytes = (long)a.hkv * DEC_D;          // bytes between consecutive slots of a page
+  const long row_bytes = (long)a.hkv * D;              // bytes between consecutive slots of a page
 
   // byte offset of 16-token block i of the chunk (lane i; blocks past the
   // end repeat the last valid block so every address stays inside the cache)
@@ -81,7 +94,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
     const int i = min(lane, nblk - 1);
     const int tb = t_begin + 16 * i;
     const int page = clampi(a.kv_indices[p0 + tb / ps], 0, a.num_pages - 1);
-    boff = ((long)page * ps + tb % ps) * row_bytes + (long)hk * DEC_D;
+    boff = ((long)page * ps + tb % ps) * row_bytes + (long)hk * D;
   }
   const uint32_t boff_lo = (uint32_t)boff, boff_hi = (uint32_t)(boff >> 32);
   auto blk_off = [&](int i) -> long {  // wave-uniform
@@ -92,12 +105,12 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
 
   // Q^T operand: lane (n, g) holds q head hk*G + n, d in [64(m/2) + 16g + 8(m%2), +8)
   // for MFMA m (the K operand below uses the same d order)
-  v8bf qop[4];
+  v8bf qop[NM];
   {
     const bool have = n < G;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)b * a.hq + hk * G + n) * DEC_D + 16 * g;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)b * a.hq + hk * G + n) * D + 16 * g;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < NM; ++m) {
       const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 64 * (m >> 1) + 8 * (m & 1)) : u32x4{0u, 0u, 0u, 0u};
       qop[m] = __builtin_bit_cast(v8bf, w);
     }
@@ -105,9 +118,10 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
   const float kfold = a.sm_scale_log2 * a.k_scale[hk];
   const float vsc = a.v_scale[hk];
 
-  // K of one step: [block][half], bytes [16g, 16g+16) and [64+16g, 64+16g+16) of
-  // token n (clamped into the block): each load reads 64 contiguous bytes per row
-  struct KRegs { u32x4 k[2][2]; };
+  // K of one step: [block][half], bytes [16g, 16g+16) (and, for D = 128,
+  // [64+16g, 64+16g+16)) of token n (clamped into the block): each load
+  // reads 64 contiguous bytes per row
+  struct KRegs { u32x4 k[2][KH]; };
   const uint32_t k_lane = (uint32_t)(n * row_bytes + 16 * g);
   auto load_k = [&](int st, KRegs& r) {
 #pragma unroll
@@ -116,26 +130,29 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
       const uint8_t* base = a.k_cache + blk_off(i);
       const int vb = blk_valid(i);
       const uint32_t off = vb == 16 ? k_lane : (uint32_t)(min(n, vb - 1) * row_bytes + 16 * g);
-      r.k[j][0] = *reinterpret_cast<const u32x4*>(base + off);
-      r.k[j][1] = *reinterpret_cast<const u32x4*>(base + off + 64);
+#pragma unroll
+      for (int h = 0; h < KH; ++h) r.k[j][h] = *reinterpret_cast<const u32x4*>(base + off + 64 * h);
     }
   };
-  // V of one step -> LDS stage: direct load i (0..3) fills tile rows 8i..8i+7
-  // (token rows of the step), lane L holds 16-byte chunk L%8 ^ swizzle of row 8i + L/8
+  // V of one step -> LDS stage: direct load i fills tile rows RPL*i .. RPL*i+RPL-1
+  // (token rows of the step; 16 rows per 16-token block), lane L holds 16-byte
+  // chunk L%CPR ^ swizzle of row RPL*i + L/CPR
   uint8_t* vst0 = s_v[wave][0];
-  uint32_t v_lane[4];
+  constexpr int LPB = 16 / RPL;                    // direct loads per 16-token block
+  uint32_t v_lane[NVL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v_lane[i] = (uint32_t)(((i & 1) * 8 + (lane >> 3)) * row_bytes + (((lane & 7) ^ dec_vsw(8 * i + (lane >> 3))) << 4));
+  for (int i = 0; i < NVL; ++i)
+    v_lane[i] = (uint32_t)(((i % LPB) * RPL + lane / CPR) * row_bytes +
+                           (((lane % CPR) ^ dec_vsw<D>(RPL * i + lane / CPR)) << 4));
   auto load_v = [&](int st, int stage) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bi = min(2 * st + (i >> 1), DEC_BLKS - 1);
+    for (int i = 0; i < NVL; ++i) {
+      const int bi = min(2 * st + i / LPB, DEC_BLKS - 1);
       const int vb = blk_valid(bi);
       uint32_t off = v_lane[i];
       if (vb < 16)  // rows past the end re-read the block's last valid token
-        off = (uint32_t)(min((i & 1) * 8 + (lane >> 3), vb - 1) * row_bytes +
-                         (((lane & 7) ^ dec_vsw(8 * i + (lane >> 3))) << 4));
+        off = (uint32_t)(min((i % LPB) * RPL + lane / CPR, vb - 1) * row_bytes +
+                         (((lane % CPR) ^ dec_vsw<D>(RPL * i + lane / CPR)) << 4));
       // descriptor over the 16 slots of this block (wave-uniform 64-bit base)
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(a.v_cache + blk_off(bi)), (short)0, (int)(16 * row_bytes), 0x00020000);
@@ -147,16 +164,16 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
   // 16*(e/4) + 4g + e%4 (the S^T accumulator order); lane k of a 16-lane group
   // supplies token slot e = k/2, bytes 8*(k%2) of the d chunk
   const int tr_row = 16 * ((n >> 1) >> 2) + 4 * g + ((n >> 1) & 3);
-  const int tr_sw = dec_vsw(tr_row);
+  const int tr_sw = dec_vsw<D>(tr_row);
   // LDS byte address (stage 0) of this lane's transposed read of d block db
-  uint32_t tra[DEC_D / 16];
+  uint32_t tra[D / 16];
 #pragma unroll
-  for (int db = 0; db < DEC_D / 16; ++db)
-    tra[db] = (uint32_t)(uintptr_t)(dec_lds_t)(vst0 + tr_row * DEC_D + 8 * (n & 1) + ((db ^ tr_sw) << 4));
+  for (int db = 0; db < D / 16; ++db)
+    tra[db] = (uint32_t)(uintptr_t)(dec_lds_t)(vst0 + tr_row * D + 8 * (n & 1) + ((db ^ tr_sw) << 4));
 
-  v4f oacc[DEC_D / 16];
+  v4f oacc[D / 16];
 #pragma unroll
-  for (int db = 0; db < DEC_D / 16; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < D / 16; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;
   const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
 
@@ -176,7 +193,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
     for (int j = 0; j < 2; ++j) {
       v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < NM; ++m) {
         const uint32_t w0 = kc.k[j][m >> 1][2 * (m & 1)], w1 = kc.k[j][m >> 1][2 * (m & 1) + 1];
         const v2bf c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
         const v2bf c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
@@ -207,7 +224,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DEC_D / 16; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
     }
     const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
     v8h pk;
@@ -222,28 +239,40 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
         l_run = __builtin_amdgcn_fdot2(ph, ones, l_run, false);
       }
     // ---- O^T += V^T P^T; the step's V stage has landed (only step st+1's
-    // eight loads may still be in flight)
-    dec_wait_vm<8>();
-    // the eight transposed reads as one block (the compiler would otherwise
-    // drain every in-flight direct load before each of them)
-    v2i raw[DEC_D / 16];
-    asm volatile(
-        "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
-        "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(raw[4]), "=&v"(raw[5]),
-          "=&v"(raw[6]), "=&v"(raw[7])
-        : "v"(tra[0]), "v"(tra[1]), "v"(tra[2]), "v"(tra[3]), "v"(tra[4]), "v"(tra[5]), "v"(tra[6]),
-          "v"(tra[7]), "i"(STAGE * DEC_VTILE)
-        : "memory");
+    // KH*2 K loads and NVL V loads may still be in flight)
+    dec_wait_vm<2 * KH + NVL>();
+    // the transposed reads as one block (the compiler would otherwise drain
+    // every in-flight direct load before each of them)
+    v2i raw[D / 16];
+    if constexpr (D == 128) {
+      asm volatile(
+          "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
+          "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3]), "=&v"(raw[4]), "=&v"(raw[5]),
+            "=&v"(raw[6]), "=&v"(raw[7])
+          : "v"(tra[0]), "v"(tra[1]), "v"(tra[2]), "v"(tra[3]), "v"(tra[4]), "v"(tra[5]), "v"(tra[6]),
+            "v"(tra[7]), "i"(STAGE * DEC_VTILE)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b8 %0, %4 offset:%8\n\t"
+          "ds_read_b64_tr_b8 %1, %5 offset:%8\n\t"
+          "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
+          "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(raw[2]), "=&v"(raw[3])
+          : "v"(tra[0]), "v"(tra[1]), "v"(tra[2]), "v"(tra[3]), "i"(STAGE * DEC_VTILE)
+          : "memory");
+    }
 #pragma unroll
-    for (int db = 0; db < DEC_D / 16; ++db) {
+    for (int db = 0; db < D / 16; ++db) {
       const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][0], 1.0f, false);
       const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][0], 1.0f, true);
       const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)raw[db][1], 1.0f, false);
@@ -276,15 +305,15 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
     const long row = ((long)b * a.hq + qh) * a.n_chunks + chunk;
     const float inv = l != 0.f ? vsc / l : 0.f;  // a NaN sum stays NaN
 #pragma unroll
-    for (int db = 0; db < DEC_D / 16; ++db)
-      *reinterpret_cast<v4f*>(a.ws_o + row * DEC_D + db * 16 + 4 * g) = oacc[db] * inv;
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<v4f*>(a.ws_o + row * D + db * 16 + 4 * g) = oacc[db] * inv;
     if (g == 0) a.ws_lse[row] = l != 0.f ? m_ref + __log2f(l) : -INFINITY;
   }
 }
 
 // Merge: O = sum_c 2^(lse_c - lse) O_c, lse = log2 sum_c 2^lse_c.  One wave
 // per (sequence, q head): lane c holds chunk c's lse (64 chunks per pass), the
-// weights come from a wave max / sum, and each lane accumulates two d values
+// weights come from a wave max / sum, and each lane accumulates D/64 d values
 // over the chunks with eight independent loads in flight.
 constexpr int MERGE_THREADS = 256;
 
@@ -294,7 +323,10 @@ ATTNQ_DEV float wave_sum(float v) {
   return v;
 }
 
+template <int D>
 __global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(const DecodeArgs a) {
+  constexpr int VPL = D / 64;  // d values per lane
+  typedef float vpl_t __attribute__((ext_vector_type(VPL)));
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6);  // b * hq + qh
   if (row >= a.batch * a.hq) return;
@@ -313,30 +345,36 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(const DecodeArgs
     m = fmaxf(m, wave_max(lc));
   }
   float tot = 0.f;
-  v2f acc = v2f{0.f, 0.f};
+  vpl_t acc = {};
   if (m != -INFINITY && !nan) {
     for (int c0 = 0; c0 < nc; c0 += 64) {
       const float lc = c0 + lane < nc ? a.ws_lse[row0 + c0 + lane] : -INFINITY;
       const float w = lc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lc - m);
       tot += wave_sum(w);
       const int cn = min(64, nc - c0);
-      const float* op = a.ws_o + (row0 + c0) * DEC_D + 2 * lane;
+      const float* op = a.ws_o + (row0 + c0) * D + VPL * lane;
       int c = 0;
       for (; c + 8 <= cn; c += 8) {
-        v2f o8[8];
+        vpl_t o8[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o8[u] = *reinterpret_cast<const v2f*>(op + (long)(c + u) * DEC_D);
+        for (int u = 0; u < 8; ++u) o8[u] = *reinterpret_cast<const vpl_t*>(op + (long)(c + u) * D);
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), c + u)) * o8[u];
       }
       for (; c < cn; ++c)
         acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), c)) *
-               *reinterpret_cast<const v2f*>(op + (long)c * DEC_D);
+               *reinterpret_cast<const vpl_t*>(op + (long)c * D);
     }
   }
   const float inv = nan ? __builtin_nanf("") : tot > 0.f ? 1.f / tot : 0.f;
-  const v2bf ob = __builtin_convertvector(acc * inv, v2bf);
-  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.o) + (long)row * DEC_D + 2 * lane) = __builtin_bit_cast(uint32_t, ob);
+  uint16_t* op = static_cast<uint16_t*>(a.o) + (long)row * D + VPL * lane;
+  if constexpr (VPL == 2) {
+    const v2bf ob = __builtin_convertvector(acc * inv, v2bf);
+    *reinterpret_cast<uint32_t*>(op) = __builtin_bit_cast(uint32_t, ob);
+  } else {
+    const v2bf ob = __builtin_convertvector(v2f{acc[0] * inv, 0.f}, v2bf);
+    *op = __builtin_bit_cast(uint16_t, ob[0]);
+  }
   if (a.lse && lane == 0)
     a.lse[row] = nan ? __builtin_nanf("") : tot > 0.f ? (m + __log2f(tot)) * DEC_LN2 : -INFINITY;
 }
@@ -353,14 +391,19 @@ size_t decode_workspace_bytes(int batch, int hq, int head_dim, int max_kv_len, i
   return rows * head_dim * sizeof(float) + rows * sizeof(float) + 256;
 }
 
-bool launch_decode(const DecodeArgs& a, hipStream_t s) {
-  if (a.batch <= 0) return true;
-  hipLaunchKernelGGL(k_decode_split, dim3(a.n_chunks, a.batch, (a.hkv + 3) / 4), dim3(DEC_THREADS), 0, s, a);
+template <int D>
+static bool launch_decode_d(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_decode_split<D>, dim3(a.n_chunks, a.batch, (a.hkv + 3) / 4), dim3(DEC_THREADS), 0, s, a);
   if (hipGetLastError() != hipSuccess) return false;
   const int rows = a.batch * a.hq;
-  hipLaunchKernelGGL(k_decode_merge, dim3((rows + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64)),
+  hipLaunchKernelGGL(k_decode_merge<D>, dim3((rows + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64)),
                      dim3(MERGE_THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
+}
+
+bool launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s) {
+  if (a.batch <= 0) return true;
+  return head_dim == 128 ? launch_decode_d<128>(a, s) : launch_decode_d<64>(a, s);
 }
 
 int decode_n_chunks(int max_kv_len) { return n_chunks_for(max_kv_len); }

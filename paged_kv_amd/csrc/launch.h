@@ -45,10 +45,13 @@ struct PrefillArgs {
   int v_chan;             // v_scale holds one descale per (sequence, kv head, channel)
   float sm_scale_log2;    // sm_scale * log2(e)
 };
-// Q/K forms of the prefill: fp8 codes with per-head descales; int8 codes with
-// per-block scales; or 16-bit Q (fp16 / bf16) that the kernel quantizes to
-// int8 per 128-query block itself, with int8 per-block K
-enum { PF_Q_FP8 = 0, PF_Q_I8 = 1, PF_Q_RAW_F16 = 2, PF_Q_RAW_BF16 = 3 };
+// Q/K forms of the prefill: fp8 codes with per-head descales (QK^T summed
+// exactly: codes widened to fp16, f16 MFMA); the same with the fp8 MFMA
+// (faster, its 128-product sums carry a relative error up to ~2^-11.8 of
+// sum |q_d k_d|); int8 codes with per-block scales; or 16-bit Q (fp16 /
+// bf16) that the kernel quantizes to int8 per 128-query block itself, with
+// int8 per-block K
+enum { PF_Q_FP8 = 0, PF_Q_I8 = 1, PF_Q_RAW_F16 = 2, PF_Q_RAW_BF16 = 3, PF_Q_FP8_MFMA8 = 4 };
 // q_mode: one of PF_Q_*; v_fp8: fp8 V (else fp16 V)
 bool launch_prefill(const PrefillArgs& a, int head_dim, int q_mode, bool v_fp8, bool o_bf16,
                     int max_seqlen_q, hipStream_t s);
@@ -72,7 +75,7 @@ struct DecodeArgs {
 size_t decode_workspace_bytes(int batch, int hq, int head_dim, int max_kv_len, int page_size);
 int decode_chunk_pages(int page_size);
 int decode_n_chunks(int max_kv_len);
-bool launch_decode(const DecodeArgs& a, hipStream_t s);
+bool launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);  // head_dim 64 or 128
 
 struct MlaArgs {
   const void* q;           // bf16 [B, Sq, H, 576]

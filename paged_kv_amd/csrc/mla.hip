@@ -9,25 +9,28 @@
 // An index entry e >= 0 names tokens [e*sbs, e*sbs + sbs); a token is used
 // if it is below kv_len and, with sparse_mode 3, at most kv_len - s_q + s.
 //
-// Split phase: one workgroup (16 waves) per (query row, 256-index split,
-// group of 64 heads).  The split's indices are resolved through block_table once,
-// into LDS.  Per 32-index step the workgroup gathers the 32 selected rows,
-// widens the codes to fp16 (exact for int8 and e4m3fn) into token-major LDS rows.  Four
-// waves serve 16 heads, split by channel tile: each owns one 128-channel tile
-// of QK and PV (the last one also the rope part) and the four exchange their
-// partial scores through LDS once per step; the PV operand (channel-major)
-// is read from the token-major rows with transposing LDS reads:
-//   S^T = K Q^T    per 128-channel tile: fp16 16x16x32 MFMA, then the tile's
-//                  scale per token in fp32; rope part: bf16 MFMA;
+// Split phase: one workgroup (16 waves) per (query row, 512-index split,
+// group of 64 heads).  The split's indices are resolved through block_table
+// once, into LDS.  Per 32-index step the workgroup gathers the 32 selected
+// rows and widens the codes to bf16 (exact for int8 and e4m3fn) into
+// token-major LDS rows.  Four waves serve 16 heads, split by channel tile:
+// each owns one 128-channel tile of QK and PV (the last one also the rope
+// part) and the four exchange their partial scores through LDS once per
+// step; the PV operand (channel-major) is read from the token-major rows
+// with transposing LDS reads:
+//   S^T = K Q^T    per 128-channel tile: bf16 16x16x32 MFMA on the exact
+//                  codes and the bf16 query, then the tile's scale per token
+//                  in fp32; rope part: bf16 MFMA;
 //   softmax per head against a lagging reference max (exact rescale only
-//   when a step's fp16 row sum leaves range), lane-local partial sums;
-//   O^T += codes^T (P * scale_t)^T   fp16 MFMA, one P operand per tile.
+//   when a step's row sum leaves [0, 2^14]), lane-local partial sums;
+//   O^T += codes^T (P * scale_t)^T   bf16 MFMA, one P operand per tile.
+// P * scale_t is rounded to bf16, whose range is fp32's: with p <= 2^14 the
+// operand stays finite for every tile scale up to 2^100 in magnitude.
 // Each split writes its normalized partial O (bf16) and log2-sum-exp; the
 // merge kernel combines the splits.
 //
-// The query's nope part is rounded to fp16 for the fp16 MFMA (exact for
-// 2^-14 <= |q| <= 65504) and the split partials of O are stored in bf16;
-// everything else is exact up to fp32 accumulation.
+// Rounding: P * scale_t to bf16 for the PV product and the split partials
+// of O to bf16; everything else is exact up to fp32 accumulation.
 #include "kcommon.h"
 #include "launch.h"
 #include "mla.h"
@@ -35,9 +38,8 @@
 namespace attnq {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int MLA_THREADS = 1024;                // 16 waves: 4 head blocks x 4 channel tiles
@@ -46,16 +48,16 @@ constexpr int MLA_STEP = 32;                     // indices per step
 constexpr int MLA_NOPE = 512, MLA_ROPE = 64, MLA_ROW = 656;
 constexpr int MLA_CPR = MLA_ROW / 16;            // 41 16-byte chunks per row
 constexpr int MLA_RAW = (MLA_STEP * MLA_CPR + MLA_THREADS - 1) / MLA_THREADS;  // 2
-constexpr int NAT_ROW = MLA_NOPE + 16;           // halfs per token row: 1056 B, 8 banks apart
+constexpr int NAT_ROW = MLA_NOPE + 16;           // bf16 per token row: 1056 B, 8 banks apart
 constexpr int ROPE_ROW = MLA_ROPE + 8;           // bf16 per rope row
 constexpr int MLA_SPLIT_TOKENS = 512;            // indices per split (16 steps)
 constexpr float MLA_LN2 = 0.69314718055994530942f;
-// a step whose fp16 partial row sum stays at or below this keeps the
-// lagging reference max (every p <= 2^14, inside fp16)
+// a step whose partial row sum stays at or below this keeps the lagging
+// reference max (every p <= 2^14)
 constexpr float MLA_TILE_SUM_MAX = 16384.0f;
 
 struct MlaStage {
-  _Float16 nat[MLA_STEP * NAT_ROW];
+  uint16_t nat[MLA_STEP * NAT_ROW];  // bf16 codes
   uint16_t rope[MLA_STEP * ROPE_ROW];
   float scale[MLA_STEP * 4];
 };
@@ -70,28 +72,29 @@ typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) lds_h4* lds_h4_ptr;
 
 // Transposed LDS read (ds_read_b64_tr_b16): inside each 16-lane group, lane
-// 4k + q names 4 consecutive fp16 values of row k; lane n receives value n
+// 4k + q names 4 consecutive 16-bit values of row k; lane n receives value n
 // of the 4 rows (column n of the 4 x 16 block).
-ATTNQ_DEV uint2 read_tr16(const _Float16* p) {
+ATTNQ_DEV uint2 read_tr16(const uint16_t* p) {
   const lds_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_ptr)(p));
   return __builtin_bit_cast(uint2, v);
 }
 
-// 4 int8 codes -> 4 fp16 values, exactly: 0x64XX is fp16 1024 + XX, and
-// XX = code + 128 after flipping the sign bit.
-ATTNQ_DEV void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+// 4 int8 codes -> 4 bf16 values, exactly (|code| <= 128 has at most 8
+// significant bits): each byte converted to fp32, pairs rounded to bf16.
+ATTNQ_DEV void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  // code + 128 as unsigned bytes, each converted exactly to fp32, minus 128;
+  // the upper halves of the fp32 values are the exact bf16 patterns
   const uint32_t u = w ^ 0x80808080u;
-  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const v2h off = v2h{(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, a) - off);
-  hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, b) - off);
+  const float f0 = (float)(u & 0xffu) - 128.0f, f1 = (float)((u >> 8) & 0xffu) - 128.0f;
+  const float f2 = (float)((u >> 16) & 0xffu) - 128.0f, f3 = (float)(u >> 24) - 128.0f;
+  lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
 
-// 4 e4m3fn codes -> 4 fp16 values (every e4m3fn value is exact in fp16).
-ATTNQ_DEV void f8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+// 4 e4m3fn codes -> 4 bf16 values (every e4m3fn value is exact in bf16).
+ATTNQ_DEV void f8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 template <bool KV_FP8>
@@ -134,8 +137,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
     }
   }
 
-  // ---- query operands of this wave's nope tile (fp16) and, for t = 3, rope (bf16)
-  v8h qn[4];
+  // ---- query operands (bf16, as given) of this wave's nope tile and, for t = 3, rope
+  v8bf qn[4];
   v8bf qr[2];
   {
     const bool have = head < a.heads;
@@ -143,13 +146,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 128 * t + 32 * g + 8 * m) : u32x4{0u, 0u, 0u, 0u};
-      v8h h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[2 * e] = (_Float16)bf16_to_f32(w[e] & 0xffffu);
-        h[2 * e + 1] = (_Float16)bf16_to_f32(w[e] >> 16);
-      }
-      qn[m] = h;
+      qn[m] = __builtin_bit_cast(v8bf, w);
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -166,7 +163,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
   // reference max (log2 units); -inf until set so the first step's p are
   // inf/NaN and force the exact path
   float m_ref = -INFINITY, l_run = 0.f;
-  const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
 
   // ---- staging: chunk c of a step = (row c % 32, 16-byte column c / 32).
   // The rows of step st + 1 are gathered into registers while step st computes.
@@ -192,8 +188,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
           uint32_t h[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if constexpr (KV_FP8) f8x4_to_f16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
-            else i8x4_to_f16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
+            if constexpr (KV_FP8) f8x4_to_bf16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
+            else i8x4_to_bf16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
           }
           u32x4* dn = reinterpret_cast<u32x4*>(&B.nat[r * NAT_ROW + col]);
           dn[0] = u32x4{h[0], h[1], h[2], h[3]};
@@ -235,8 +231,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const v8h kop = *reinterpret_cast<const v8h*>(&B.nat[(16 * j + n) * NAT_ROW + 128 * t + 32 * g + 8 * m]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qn[m], acc, 0, 0, 0);
+          const v8bf kop = *reinterpret_cast<const v8bf*>(&B.nat[(16 * j + n) * NAT_ROW + 128 * t + 32 * g + 8 * m]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qn[m], acc, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sp[j][r] = sc[j][r] * acc[r];
@@ -283,7 +279,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       const float p1 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4 + 1] - m_ref);
       p[sl] = p0;
       p[sl + 1] = p1;
-      lt = __builtin_amdgcn_fdot2(__builtin_convertvector(v2f{p0, p1}, v2h), ones, lt, false);
+      lt += p0 + p1;
     }
     if (__ballot(!(lt <= MLA_TILE_SUM_MAX))) {
       float mx = -INFINITY;
@@ -305,7 +301,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
         const float p1 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4 + 1] - mu);
         p[sl] = p0;
         p[sl + 1] = p1;
-        lt = __builtin_amdgcn_fdot2(__builtin_convertvector(v2f{p0, p1}, v2h), ones, lt, false);
+        lt += p0 + p1;
       }
     }
     l_run += lt;
@@ -313,10 +309,13 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
     // ---- O^T += codes^T (P * scale_t)^T for this wave's tile.  Slot sl of
     // lane group g is token (sl / 4) * 16 + 4g + sl % 4; the codes^T operand
     // comes from the token-major rows through two transposed reads.
-    v8h pk;
+    v8bf pk;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl)
-      pk[sl] = (_Float16)(p[sl] * sc[sl / 4][sl % 4]);
+    for (int sl = 0; sl < 8; sl += 2) {
+      const v2bf pb = __builtin_convertvector(v2f{p[sl] * sc[sl / 4][sl % 4], p[sl + 1] * sc[sl / 4][sl % 4 + 1]}, v2bf);
+      pk[sl] = pb[0];
+      pk[sl + 1] = pb[1];
+    }
     // address lane (g, 4k + q) names token (4g + k) (+16), channels 4q..4q+3 of the d-block
     const int tr_row = 4 * g + (n >> 2), tr_col = 4 * (n & 3);
 #pragma unroll
@@ -324,8 +323,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       const int c0 = 128 * t + 16 * db + tr_col;
       const uint2 lo = read_tr16(&B.nat[tr_row * NAT_ROW + c0]);
       const uint2 hi = read_tr16(&B.nat[(16 + tr_row) * NAT_ROW + c0]);
-      const v8h vop = __builtin_bit_cast(v8h, u32x4{lo.x, lo.y, hi.x, hi.y});
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[db], 0, 0, 0);
+      const v8bf vop = __builtin_bit_cast(v8bf, u32x4{lo.x, lo.y, hi.x, hi.y});
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pk, oacc[db], 0, 0, 0);
     }
     __syncthreads();  // step st + 1 staged; exchange buffer free again
   }

@@ -5,19 +5,24 @@
 // prefill; aiter's fp8 flash_attn_func with q/k/v descales; PaddleNLP's Sage
 // attention over a varlen batch with per-block int8 Q/K).
 //
-// Work split: one workgroup (4 waves) per (sequence, q head, 128-query tile); the grid's y
-// index runs over query tiles from the end of the sequence (the tiles with
-// the most visible keys start first).  Each wave owns 32 queries and streams
-// 64-key tiles staged in LDS by direct loads (three-stage ring).
+// Work split: one workgroup (4 waves) per (sequence, q head, 128-query tile)
+// on a 1-D grid whose order (pf_work_item) starts the tiles with the most
+// visible keys first and keeps the q heads of one kv head on one XCD.  Each
+// wave owns 32 queries and streams 64-key tiles staged in LDS by direct
+// loads (three-stage ring).
 //
 // Per key tile and wave:
-//   S^T = K Q^T          fp8 16x16x128 MFMA (or two int8 16x16x64), fp32/i32 acc;
-//                        the codes' scales and sm_scale*log2(e) are folded into
-//                        one multiplier per tile;
-//   online softmax       row max across the 4 lanes that hold one query, one
-//                        fma + exp2 per score, the reference max moved only when
-//                        a row max grows by more than 2^8 (then O and l rescale);
-//                        row sums by dot2 over the fp16 P fed to the PV MFMA;
+//   S^T = K Q^T          fp8 codes widened to fp16 (exact) and f16 16x16x32
+//                        MFMAs (an fp32-exact sum; the fp8 16x16x128 MFMA sums
+//                        its 128 products to only ~2^-12 of sum |q_d k_d|,
+//                        available as a separate Q/K form), or two int8
+//                        16x16x64 (exact i32); the codes' scales and
+//                        sm_scale*log2(e) are folded into one multiplier per tile;
+//   online softmax       one fma + exp2 per score against a lagging reference
+//                        max, moved (tile max across the 4 lanes that hold one
+//                        query; O and l rescale) only when a tile's partial
+//                        row sum leaves [0, 2^14]; row sums by dot2 over the
+//                        fp16 P fed to the PV MFMA;
 //   O^T += V^T P^T       fp16 16x16x32 MFMA; P is rounded to fp16, fp8 V codes
 //                        are widened to fp16 (exactly) when staged into LDS.
 // Because S^T's accumulator layout (lane n of each 16-lane row holds query n,
@@ -116,6 +121,15 @@ ATTNQ_DEV void pf_widen_fp8(const u32x4 w, u32x4& lo, u32x4& hi) {
   hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[3], 1.0f, true));
 }
 
+// 8 fp8 codes (two dwords) -> 8 fp16 values (exact).
+ATTNQ_DEV v8h pf_widen8(uint32_t w0, uint32_t w1) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Direct loads of one tile: K rows into the K stage and (fp16 V) V^T rows into
 // the V stage; this wave's share is blocks [wave*N, wave*N + N) of 1 KB.
 template <int D, bool V_F8>
@@ -173,7 +187,8 @@ ATTNQ_DEV void pf_work_item(const PrefillArgs& a, int ntiles, int lin, int& b, i
 template <int D, int QM, bool V_F8, bool O_BF16>
 __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const PrefillArgs a) {
   using G = PfGeo<D, V_F8>;
-  constexpr bool QK_I8 = QM != PF_Q_FP8;                     // int8 QK MFMA
+  constexpr bool QK_F8 = QM == PF_Q_FP8 || QM == PF_Q_FP8_MFMA8;  // fp8 codes
+  constexpr bool QK_I8 = !QK_F8;                             // int8 QK MFMA
   constexpr bool Q_RAW = QM == PF_Q_RAW_F16 || QM == PF_Q_RAW_BF16;  // Q quantized here
   // the DMA ring, then 4 floats for the block-amax exchange of a raw Q
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS + 16];
@@ -236,6 +251,16 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   // loop, drains the next tile's loads before every tile's first MFMA.  (A raw
   // Q is waited for after the first tiles' loads are issued, below.)
   if constexpr (!Q_RAW) pf_wait_vm<0>();
+  // fp8 codes summed exactly: the lane's QB codes of each query row as
+  // QB/8 fp16 operands of 8 (codes 8m .. 8m+7 of its bytes)
+  v8h q16[2][QB / 8];
+  if constexpr (QM == PF_Q_FP8) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int m = 0; m < QB / 8; ++m)
+        q16[qb][m] = pf_widen8((uint32_t)qop[qb][m >> 1][2 * (m & 1)], (uint32_t)qop[qb][m >> 1][2 * (m & 1) + 1]);
+  }
 
   float q_sc = 1.0f;
   if constexpr (Q_RAW) {
@@ -421,6 +446,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
       const v4i ka = *reinterpret_cast<const v4i*>(sk + kb * 16 * D + kr0);
       v4i kb2 = v4i{0, 0, 0, 0};
       if constexpr (QB == 32) kb2 = *reinterpret_cast<const v4i*>(sk + kb * 16 * D + kr1);
+      v8h kw16[QB / 8];  // this key's codes as fp16, the layout of q16
+      if constexpr (QM == PF_Q_FP8) {
+#pragma unroll
+        for (int m = 0; m < QB / 8; ++m) {
+          const v4i src = m < 2 ? ka : kb2;
+          kw16[m] = pf_widen8((uint32_t)src[2 * (m & 1)], (uint32_t)src[2 * (m & 1) + 1]);
+        }
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if constexpr (QK_I8) {
@@ -445,7 +478,16 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
           const v8i qo = v8i{qop[qb][0][0], qop[qb][0][1], qop[qb][0][2], qop[qb][0][3],
                              qop[qb][1][0], qop[qb][1][1], qop[qb][1][2], qop[qb][1][3]};
           v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qo, acc, 0, 0, 0, 0, 0, 0);
+          if constexpr (QM == PF_Q_FP8_MFMA8) {
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qo, acc, 0, 0, 0, 0, 0, 0);
+          } else {
+            // the lane's QB codes of key n and query n, 8 at a time: the same
+            // dims for both operands of each f16 MFMA (the order of the terms
+            // over the MFMAs does not change the sum)
+#pragma unroll
+            for (int m = 0; m < QB / 8; ++m)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kw16[m], q16[qb][m], acc, 0, 0, 0);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[kb][qb][r] = acc[r];
         }
@@ -466,7 +508,11 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     else
       fold = base_fold * k_sc_head;
 
-    // ---- mask (only tiles that cross the causal diagonal or the sequence end)
+    // ---- mask (only tiles that cross the causal diagonal or the sequence
+    // end): the fold is applied first and the scaled logit of a key past the
+    // row's limit becomes -inf by select, so the mask holds for any fold
+    // (sm_scale <= 0, scales of either sign) and NaN garbage in a masked key
+    // cannot leak.  Such a tile then continues with a unit fold.
     const bool need_mask = kfirst + PF_BN > min(Lk, wq0 + off + 1);
     if (need_mask) {
 #pragma unroll
@@ -476,8 +522,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kfirst + kb * 16 + 4 * g + r;
-            s[kb][qb][r] = key < lim[qb] ? s[kb][qb][r] : -INFINITY;
+            s[kb][qb][r] = key < lim[qb] ? s[kb][qb][r] * fold : -INFINITY;
           }
+      fold = 1.0f;
     }
 
     // ---- online softmax against a lagging reference max.  Common path:
@@ -508,14 +555,15 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     if (__ballot(redo)) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        // the row's largest scaled logit in this tile (masked keys are -inf)
         float m = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][qb][r]);
+          for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][qb][r] * fold);
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float m_new = fmaxf(m_ref[qb], m * fold);  // fold > 0
+        const float m_new = fmaxf(m_ref[qb], m);
         const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
         l_run[qb] *= alpha;
@@ -550,6 +598,10 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
           oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db][ks], pk[qb][ks], oacc[db][qb], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   }
+  // No direct load may outlive the workgroup's LDS.  The last tile waits for
+  // every load it issued; this covers a workgroup whose loop never ran (no
+  // visible key: n_kt == 0) after the raw-Q prologue issued two tiles anyway.
+  pf_wait_vm<0>();
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
   // V descale: fp8 codes, or fp16 values that carry one (the widened codes)
@@ -611,6 +663,7 @@ template <int D>
 static bool launch_q(const PrefillArgs& a, int q_mode, bool v_fp8, bool o_bf16, int max_seqlen_q, hipStream_t s) {
   switch (q_mode) {
     case PF_Q_FP8: return launch_v<D, PF_Q_FP8>(a, v_fp8, o_bf16, max_seqlen_q, s);
+    case PF_Q_FP8_MFMA8: return launch_v<D, PF_Q_FP8_MFMA8>(a, v_fp8, o_bf16, max_seqlen_q, s);
     case PF_Q_I8: return launch_v<D, PF_Q_I8>(a, v_fp8, o_bf16, max_seqlen_q, s);
     case PF_Q_RAW_F16: return launch_v<D, PF_Q_RAW_F16>(a, v_fp8, o_bf16, max_seqlen_q, s);
     case PF_Q_RAW_BF16: return launch_v<D, PF_Q_RAW_BF16>(a, v_fp8, o_bf16, max_seqlen_q, s);

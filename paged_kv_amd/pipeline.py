@@ -8,8 +8,6 @@ tensors already on the GPU, with the dtypes named in include/attnq.h
 """
 from __future__ import annotations
 
-import math
-
 import torch
 
 from . import api as A
@@ -17,6 +15,11 @@ from . import api as A
 
 def _round_up(x: int, m: int) -> int:
     return (x + m - 1) // m * m
+
+
+def _scale(sm_scale) -> float:
+    """None selects the library's default scale 1/sqrt(d_k) (passed as NaN)."""
+    return float("nan") if sm_scale is None else float(sm_scale)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -31,21 +34,24 @@ class Fp8Prefill:
     """fp8 per-head quantization of Q/K/V followed by the varlen prefill
     (the aiter fp8 flash_attn_func flow over a ragged batch).  With
     wide_v (default) the permuted V holds each fp8 code's exact fp16 value,
-    which the prefill stages without a widening step."""
+    which the prefill stages without a widening step.  QK^T is summed
+    exactly from the codes; fp8_mma8 selects the fp8 matrix instruction
+    instead (faster, with its documented accumulation error)."""
 
     def __init__(self, q, k, v, cu_seqlens, max_seqlen, sm_scale, causal=True,
-                 out_dtype=torch.bfloat16, want_lse=False, amax=None, wide_v=True):
+                 out_dtype=torch.bfloat16, want_lse=False, amax=None, wide_v=True, fp8_mma8=False):
         dev = q.device
         self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
         self.t, self.hq, self.d = q.shape
         self.hkv = k.shape[1]
         self.b = cu_seqlens.numel() - 1
         self.max_seqlen = int(max_seqlen)
-        self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        self.sm_scale, self.causal = _scale(sm_scale), bool(causal)
         self.amax = amax  # optional (amax_q, amax_k, amax_v) from the append step
         self.qc = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         self.kc = torch.empty(k.shape, dtype=torch.uint8, device=dev)
         self.wide_v = bool(wide_v)
+        self.qk_mode = A.Q_FP8_PER_HEAD_MFMA8 if fp8_mma8 else A.Q_FP8_PER_HEAD
         self.vp = torch.empty((self.b, self.hkv, self.d, _round_up(self.max_seqlen, 128)),
                               dtype=torch.float16 if self.wide_v else torch.uint8, device=dev)
         self.qs = torch.empty(self.hq, dtype=torch.float32, device=dev)
@@ -68,7 +74,7 @@ class Fp8Prefill:
     def attend(self):
         A.attn_prefill_varlen(self.qc, self.kc, self.vp, A.FP8E4M3,
                               A.FP16 if self.wide_v else A.FP8E4M3, self.qs, self.ks,
-                              self.vs, A.Q_FP8_PER_HEAD, A.Q_FP8_PER_HEAD, self.cu, self.cu, self.b, self.max_seqlen,
+                              self.vs, A.Q_FP8_PER_HEAD, self.qk_mode, self.cu, self.cu, self.b, self.max_seqlen,
                               self.max_seqlen, self.t, self.t, self.hq, self.hkv, self.d,
                               self.sm_scale, self.causal, self.o, _dtype_code(self.o), self.lse)
 
@@ -99,7 +105,7 @@ class SagePrefill:
         self.hkv = k.shape[1]
         self.b = cu_seqlens.numel() - 1
         self.max_seqlen = int(max_seqlen)
-        self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        self.sm_scale, self.causal = _scale(sm_scale), bool(causal)
         self.fuse_q = bool(fuse_q)
         self.smooth_k = bool(smooth_k)
         self.v_chan = bool(v_fp8_per_channel)
@@ -159,7 +165,8 @@ class AppendRopeFp8Prefill:
     prefill on the rotated Q/K and V (the long-context flow)."""
 
     def __init__(self, q, k, v, cu_seqlens, kv_len_before, max_seqlen, rope_cos_sin, k_cache,
-                 v_cache, kv_indptr, kv_indices, page_size, sm_scale, causal=True, want_lse=False):
+                 v_cache, kv_indptr, kv_indices, page_size, sm_scale, causal=True, want_lse=False,
+                 fp8_mma8=False):
         dev = q.device
         self.q, self.k, self.v = q, k, v
         self.cu, self.before = cu_seqlens, kv_len_before
@@ -171,7 +178,7 @@ class AppendRopeFp8Prefill:
         self.amax = tuple(torch.empty(h, dtype=torch.float32, device=dev)
                           for h in (self.hq, self.hkv, self.hkv))
         self.prefill = Fp8Prefill(q, k, v, cu_seqlens, max_seqlen, sm_scale, causal,
-                                  want_lse=want_lse, amax=self.amax)
+                                  want_lse=want_lse, amax=self.amax, fp8_mma8=fp8_mma8)
 
     def append(self):
         A.attn_append_kv_rope(self.q, self.k, self.v, _dtype_code(self.q), self.cu, self.before,
@@ -204,7 +211,7 @@ class PagedPrefill:
         self.b = cu_q.numel() - 1
         self.max_q, self.max_k = int(max_q), int(max_k)
         self.tk = int(cu_k[-1].item())
-        self.sm_scale, self.causal = float(sm_scale), bool(causal)
+        self.sm_scale, self.causal = _scale(sm_scale), bool(causal)
         self.kg = torch.empty((self.tk, self.hkv, self.d), dtype=k_cache.dtype, device=dev)
         self.vg = torch.empty_like(self.kg)
         self.qc = torch.empty(q.shape, dtype=torch.uint8, device=dev)
@@ -253,7 +260,7 @@ class PagedDecode:
         self.args = (q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len)
         self.b, self.hq, self.d = q.shape
         self.num_pages, self.page_size, self.hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
-        self.max_kv_len, self.sm_scale = int(max_kv_len), float(sm_scale)
+        self.max_kv_len, self.sm_scale = int(max_kv_len), _scale(sm_scale)
         self.ws_bytes = A.attn_decode_paged_workspace_size(self.b, self.hq, self.d, self.max_kv_len,
                                                            self.page_size)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -280,7 +287,7 @@ class SparseMlaDecode:
         self.topk = sparse_indices.shape[-1]
         self.kv_dtype = A.FP8E4M3 if kv_fp8 else A.INT8
         self.sbs, self.mode = int(sparse_block_size), int(sparse_mode)
-        self.sm_scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(dq)
+        self.sm_scale = _scale(sm_scale)
         self.ws_bytes = A.attn_sparse_mla_decode_workspace_size(self.b, self.sq, self.h, self.topk, self.sbs)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.o = torch.empty((self.b, self.sq, self.h, 512), dtype=torch.bfloat16, device=dev)

@@ -15,12 +15,21 @@ import numpy as np
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-# lse (natural log) bound: 1e-3 absolute plus a relative term.  gfx950's fp8
-# MFMA sums its 128 products with about 2^-12.7 relative precision (measured
-# worst case 1.45e-4 of the sum of |products|), so logits -- and the lse of
-# rows dominated by large logits -- carry a relative error of that order.
+# lse (natural log) bound: 1e-3 absolute plus a relative term.  The absolute
+# part covers the fp16 rounding of the P that the row sums are taken over
+# (at most 2^-12 relative in l, 2.4e-4 in ln l).  Every default path sums
+# QK^T exactly up to fp32 accumulation (int8 MFMA; fp8 and int8 codes widened
+# to fp16 / bf16 for f16 / bf16 MFMA), so its relative term only covers the
+# fp32 roundings of m and ln 2 at very large logits: LSE_REL = 1e-5.
+# The opt-in fp8-MFMA QK mode (ATTNQ_Q_FP8_PER_HEAD_MFMA8) does not sum its
+# 128 products in full fp32: tests/test_gpu_mfma_accum.py measures the error
+# of q . k against exact host sums and asserts it stays within 2^-11.5 of
+# sum_d |q_d k_d|.  Its logits -- and the lse of rows dominated by large
+# logits, where sum |q_d k_d| is close to |lse| -- carry a relative error of
+# that order: LSE_REL_MFMA8 = 4e-4, that bound with a margin of 1.16.
 LSE_ABS = 1e-3
-LSE_REL = 4e-4
+LSE_REL = 1e-5
+LSE_REL_MFMA8 = 4e-4
 
 
 def to_dev(x, torch_dtype=None):
@@ -78,13 +87,13 @@ def compare_outputs(got: np.ndarray, want_rounded: np.ndarray, want_exact: np.nd
     return stats
 
 
-def compare_lse(got: np.ndarray, want: np.ndarray, label: str = "") -> float:
+def compare_lse(got: np.ndarray, want: np.ndarray, label: str = "", rel: float = LSE_REL) -> float:
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     fin = np.isfinite(want)
     assert np.array_equal(fin, np.isfinite(got)), f"{label}: lse finiteness differs"
     assert np.all(got[~fin] == want[~fin]), f"{label}: -inf rows differ"
     err = np.abs(got[fin] - want[fin])
-    tol = LSE_ABS + LSE_REL * np.abs(want[fin])
+    tol = LSE_ABS + rel * np.abs(want[fin])
     assert np.all(err <= tol), f"{label}: lse max err {err.max()} (worst ratio to bound {(err / tol).max():.3g})"
     return float(err.max(initial=0.0))

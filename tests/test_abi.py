@@ -108,7 +108,9 @@ def test_prefill_validation():
     assert _prefill(qk=pk.INT8) == -2            # int8 codes need per-block scales
     assert _prefill(vd=pk.BF16) == -2
     assert _prefill(od=pk.FP8E4M3) == -2
-    assert _prefill(sc=float("inf")) == -1
+    assert _prefill(sc=float("inf")) == -1 and "sm_scale" in _err()
+    # NaN selects the default 1/sqrt(head_dim): validation goes on to the next argument
+    assert _prefill(sc=float("nan"), cq=None) == -1 and "cu_seqlens_q" in _err()
     assert _prefill(cq=None) == -1
     assert _prefill(vs=None) == -1 and "v_scale" in _err()
     assert _prefill(mk=1 << 21, hkv=8, hq=8) == -2 and "2 GiB" in _err()   # 32-bit tile offsets
@@ -132,8 +134,10 @@ def _decode(**kw):
 def test_decode_validation():
     assert _decode(ps=8) == -1 and "page_size" in _err()
     assert _decode(ps=2048) == -1
-    assert _decode(d=64) == -2
+    assert _decode(d=96) == -2 and "head_dim" in _err()
     assert _decode(hq=32, hkv=1) == -2
+    assert _decode(sc=float("inf")) == -1 and "sm_scale" in _err()
+    assert _decode(sc=float("nan"), b=0) == 0      # default scale; nothing to do
     assert _decode(wsb=16) == -3 and "workspace" in _err()
     need = pk.attn_decode_paged_workspace_size(2, 32, 128, 100, 16)
     assert need > 0
@@ -193,6 +197,8 @@ def test_mla_validation():
     assert _mla(sbs=3) == -2 and "sparse_block_size" in _err()
     assert _mla(sbs=32) == -2
     assert _mla(mode=1) == -2 and "sparse_mode" in _err()
+    assert _mla(sc=float("-inf")) == -1 and "sm_scale" in _err()
+    assert _mla(sc=float("nan"), b=0) == 0         # default 1/sqrt(576); nothing to do
     L = pk.lib()
     assert L.attn_sparse_mla_decode_workspace_size(1, 1, 16, 8, 3) == 0
     assert L.attn_sparse_mla_decode_workspace_size(1, 1, 16, 300, 4) == L.attn_sparse_mla_decode_workspace_size(1, 1, 16, 1200, 1)

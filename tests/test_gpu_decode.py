@@ -67,13 +67,10 @@ def test_decode_page_permutation_bit_identical():
     assert np.array_equal(from_dev_bits(_run(y, 0.1).o), a)
 
 
-def test_config3_full_size_sampled():
+def test_config3_full_size():
     """Paged fp8 decode at full size (B=64, kv lens U{1024..32768}, page 16,
-    32/8 heads): every output row checked for finiteness, sampled sequences
-    (incl. the shortest and the longest) against the oracle."""
+    32/8 heads): every sequence and head against the oracle."""
     x = gen.config3()
-    lens = x["kv_lens"]
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63})
-    p, st = _check(x, x["sm_scale"], batches=pick, label="config3")
+    p, st = _check(x, x["sm_scale"], label="config3")
     assert torch.isfinite(p.o.float()).all()
-    print("config3", st)
+    print("PARITY config3 (all 64 sequences):", st)

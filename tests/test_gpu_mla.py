@@ -64,11 +64,11 @@ def test_mla_index_order_invariance():
     assert np.abs(a - b).max() <= 2e-2 and np.abs(a - b).mean() <= 2e-3
 
 
-def test_config4_full_size_sampled():
+def test_config4_full_size():
     """The sparse MLA workload at full size (B=32, 128 heads, 65536-token
     caches in 64-token blocks, 2048 distinct indices, NaN in every
-    unselected row): sampled batches against the oracle, all outputs finite."""
+    unselected row): every batch and head against the oracle."""
     x = gen.config4()
-    p, st = _check(x, x["sm_scale"], batches=[0, 7, 31], label="config4")
+    p, st = _check(x, x["sm_scale"], label="config4")
     assert torch.isfinite(p.o.float()).all()
-    print("config4", st)
+    print("PARITY config4 (all 32 batches):", st)
