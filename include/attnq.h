@@ -299,6 +299,27 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       size_t workspace_bytes, void* o, float* lse, hipStream_t stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code recorded under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and results.  The split partials go to a fixed
+ * scratch array inside the library (80 MiB per device, held from the first
+ * call on a device until the process ends); no call allocates or frees
+ * anything.  Sizes whose partials, attn_decode_paged_workspace_size(...),
+ * exceed 80 MiB return ATTNQ_EWORKSPACE with a message (80 MiB holds
+ * 64 sequences x 32 q heads of 32K-token caches at head_dim 128).  Every call
+ * on one device shares that device's scratch: calls that may overlap on one
+ * device (several streams or threads) race and must be serialized by the
+ * caller.  Nothing in the scratch needs clearing between calls.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
+                              int num_pages, int page_size, int num_q_heads, int num_kv_heads,
+                              int head_dim, int max_kv_len, float sm_scale, void* o, float* lse,
+                              hipStream_t stream);
+
+/*
  * attn_sparse_mla_decode -- MLA-absorb sparse attention over int8 or fp8 cache
  * rows with per-token tile-128 scales (Ascend "KvQuantSparseFlashAttention":
  * attention_mode 2, quant_scale_repo_mode 1, tile_size 128, rope_head_dim 64,

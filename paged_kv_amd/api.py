@@ -19,7 +19,7 @@ __all__ = [
     "library_path", "lib", "abi_version",
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
     "attn_smooth_quant_k", "attn_gather_paged_kv", "attn_decode_paged_workspace_size",
-    "attn_decode_paged",
+    "attn_decode_paged", "attn_decode_paged_noalloc",
     "attn_sparse_mla_decode_workspace_size", "attn_sparse_mla_decode", "attn_quant_kv",
     "SYMBOLS",
 ]
@@ -49,6 +49,8 @@ SYMBOLS = {
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                _P, _Z, _P, _P, _P]),
+    "attn_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                       _P, _P, _P]),
     "attn_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "attn_sparse_mla_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
                                     _P, _P, _P]),
@@ -189,6 +191,18 @@ def attn_decode_paged(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indic
                                    num_q_heads, num_kv_heads, head_dim, max_kv_len,
                                    float(sm_scale), _ptr(workspace), int(workspace_bytes), _ptr(o),
                                    _ptr(lse), s), "attn_decode_paged")
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices,
+                              kv_last_page_len, batch, num_pages, page_size, num_q_heads, num_kv_heads,
+                              head_dim, max_kv_len, sm_scale, o, lse=None, stream=None):
+    s = _stream(stream, q, o)
+    _check(lib().attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(kv_indptr), _ptr(kv_indices),
+                                           _ptr(kv_last_page_len), batch, num_pages, page_size,
+                                           num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                                           float(sm_scale), _ptr(o), _ptr(lse), s),
+           "attn_decode_paged_noalloc")
 
 
 def attn_sparse_mla_decode_workspace_size(batch, s_q, num_heads, topk, sparse_block_size=1) -> int:

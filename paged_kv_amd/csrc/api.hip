@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/attnq.h"
@@ -366,6 +367,43 @@ size_t attn_decode_paged_workspace_size(int batch, int num_q_heads, int head_dim
   return attnq::decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len, page_size);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of attn_decode_paged_noalloc: the split partials live in this
+// fixed device array instead of a caller workspace.  Each device holds its
+// own copy for the life of the process; host code reaches it only through
+// the address hipGetSymbolAddress returns on that device (the array's name
+// is a host-side stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = size_t(80) << 20;
+__device__ __align__(256) static uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(ATTNQ_ELAUNCH, "no usable current device for the library scratch (device %d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(ATTNQ_ELAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTNQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
                       const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
@@ -415,6 +453,28 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.sm_scale_log2 = sm_scale * LOG2E;
   LAUNCHED(attnq::launch_decode(a, head_dim, stream));
   return ok();
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
+                              int num_pages, int page_size, int num_q_heads, int num_kv_heads,
+                              int head_dim, int max_kv_len, float sm_scale, void* o, float* lse,
+                              hipStream_t stream) {
+  // the partials need no clearing: the merge reads exactly the chunks the
+  // split phase of this call writes
+  const size_t need = attn_decode_paged_workspace_size(batch, num_q_heads, head_dim, max_kv_len, page_size);
+  REQUIRE(need <= kNoAllocScratchBytes, ATTNQ_EWORKSPACE,
+          "attn_decode_paged_noalloc: the split partials need %zu bytes, more than the library's fixed "
+          "scratch of %zu bytes (use attn_decode_paged with a workspace)", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (batch > 0) {
+    const int st = scratch_address(&ws);
+    if (st != ATTNQ_OK) return st;
+  }
+  return attn_decode_paged(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len,
+                           batch, num_pages, page_size, num_q_heads, num_kv_heads, head_dim, max_kv_len,
+                           sm_scale, ws, kNoAllocScratchBytes, o, lse, stream);
 }
 
 // ---------------------------------------------------------------- attn_sparse_mla_decode
