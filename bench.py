@@ -17,10 +17,13 @@ its own, each with the oracle timed beside it on a bounded sample.
 ``roofline``: the prefill kernel alone, timed with HIP events on the stream
 it is launched on, against the MFMA peak of its two contractions (int8 QK at
 5.0 POP/s, fp16 PV at 2.5 PFLOP/s: 2 / (1/5000 + 1/2500) = 3333 TFLOP/s for
-equal flop counts).  ``traffic``: HBM-side bytes of one launch from two
-rocprofv3 counter runs of ``bench.py --traffic-probe`` (FETCH_SIZE, then
-WRITE_SIZE), each scaled by what the same counter reads for a device copy of
-known size; ``bench.py --summarize-traffic`` stores them under profiles/
+equal flop counts); the extra workloads carry roofline objects of their own
+(decode and sparse MLA against 8 TB/s, the long fp8 prefill against the f16
+MFMA peak of its exact QK and PV).  ``traffic``: HBM-side bytes of one
+launch from rocprofv3 counter runs of ``bench.py --counter-probe WL``
+(FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for
+a device copy of known size; ``bench.py --summarize-counters WL DIR`` writes
+them, with the MFMA-busy and instruction-mix passes, to profiles/ together
 with a hash of the kernel sources, and the figure is reported only while
 that hash matches.  ``cpu_baseline``: the fp64 oracle on a bounded sample
 of the same workload, on the host cores.
@@ -47,8 +50,6 @@ PEAK_F16 = 2500.0        # TFLOP/s dense
 PEAK_HBM = 8000.0        # GB/s
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_prefill_sage_varlen.md")
-TRAFFIC_SOURCES = ("paged_kv_amd/csrc/prefill.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")
 CALIB_BYTES = 256 << 20  # device-to-device copy used to scale the counters
 
 
@@ -183,7 +184,11 @@ def bench_config3(iters, cpu=False):
     med = float(np.median(ms))
     gbs = (kv_bytes + other) / (med * 1e-3) / 1e9
     r = {"ms": med, "ms_min": float(np.min(ms)), "bytes": kv_bytes + other, "GB/s": gbs,
-         "pct_hbm": 100 * gbs / PEAK_HBM}
+         "pct_hbm": 100 * gbs / PEAK_HBM,
+         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s", "frac": gbs / PEAK_HBM,
+                      "traffic": stored_counters("c3").get("traffic_bytes_per_launch"),
+                      "kernel": "k_decode_split<128> + k_decode_merge<128> (caches evicted before each call)",
+                      "per_launch_bytes": kv_bytes + other, "avg_launch_ms": float(np.mean(ms))}}
     if cpu:
         r["cpu_oracle"] = oracle_config3(x)
     return r
@@ -214,10 +219,27 @@ def bench_config5(iters, cpu=False):
         p.k.copy_(k0)
     pipe = time_events(p.run, max(2, iters // 2), restore)
     med = float(np.median(kms))
-    r = {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
-         "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
+    # the same launch with QK^T on the fp8 matrix instruction (opt-in mode,
+    # outside the output tolerance on this workload's outlier rows)
+    import paged_kv_amd.api as A
+    pf = p.prefill
+
+    def attend_mma8():
+        A.attn_prefill_varlen(pf.qc, pf.kc, pf.vp, A.FP8E4M3, A.FP16, pf.qs, pf.ks, pf.vs, A.Q_FP8_PER_HEAD,
+                              A.Q_FP8_PER_HEAD_MFMA8, pf.cu, pf.cu, pf.b, pf.max_seqlen, pf.max_seqlen, pf.t, pf.t,
+                              pf.hq, pf.hkv, pf.d, pf.sm_scale, pf.causal, pf.o, A.BF16, pf.lse)
+    fast = float(np.median(time_events(attend_mma8, iters)))
+    tf = flops / (med * 1e-3) / 1e12
+    r = {"prefill_ms": med, "prefill_TFLOPS": tf,
+         "pct_fp8_peak": 100 * tf / PEAK_FP8,
          "pipeline_ms": float(np.median(pipe)),
-         "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12}
+         "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12,
+         "prefill_fp8_mfma_qk_ms": fast, "prefill_fp8_mfma_qk_TFLOPS": flops / (fast * 1e-3) / 1e12,
+         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_F16, "unit": "TFLOP/s", "frac": tf / PEAK_F16,
+                      "traffic": stored_counters("c5").get("traffic_bytes_per_launch"),
+                      "mfma_util_pct": stored_counters("c5").get("mfma_util_pct"),
+                      "kernel": "k_prefill<128, fp8 codes summed exactly on f16 MFMA, fp16 V, bf16 O>",
+                      "per_launch_flop": flops, "avg_launch_ms": float(np.mean(kms))}}
     if cpu:
         r["cpu_oracle"] = oracle_config5(x)
     return r
@@ -231,7 +253,7 @@ def bench_config4(iters, cpu=False):
     x = gen.config4()
     p = SparseMlaDecode(to_dev(x["q"]), to_dev(x["kv_cache"]), to_dev(x["block_table"]),
                         to_dev(x["kv_lens"]), to_dev(x["sparse_indices"]), x["sm_scale"])
-    nbytes = 32 * 2048 * 656 + 32 * 128 * 576 * 2 + 32 * 128 * 512 * 2 + 32 * 2048 * 4 + 32 * 1024 * 4
+    nbytes = C4_BYTES
     flops = 32 * 128 * 2048 * 2.0 * (576 + 512)
     p.run()
     torch.cuda.synchronize()
@@ -240,7 +262,12 @@ def bench_config4(iters, cpu=False):
     med = float(np.median(ms))
     gbs = nbytes / (med * 1e-3) / 1e9
     r = {"ms": med, "ms_min": float(np.min(ms)), "bytes": nbytes, "GB/s": gbs,
-         "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12}
+         "pct_hbm": 100 * gbs / PEAK_HBM, "TFLOPS": flops / (med * 1e-3) / 1e12,
+         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s", "frac": gbs / PEAK_HBM,
+                      "traffic": stored_counters("c4").get("traffic_bytes_per_launch"),
+                      "mfma_util_pct": stored_counters("c4").get("mfma_util_pct"),
+                      "kernel": "sparse MLA split + merge (caches evicted before each call)",
+                      "per_launch_bytes": nbytes, "avg_launch_ms": float(np.mean(ms))}}
     if cpu:
         r["cpu_oracle"] = oracle_config4(x)
     del p, x
@@ -412,34 +439,130 @@ def oracle_config5(x, budget_s=4.0):
                       f"{t:.1f} s (RoPE + quantization {t_prep:.1f} s not counted)"}
 
 
-def kernel_source_hash() -> str:
+# ---------------------------------------------------------------------------
+# rocprofv3 counter evidence: one probe per workload (a calibration copy and
+# one launch of the workload's hot kernels), several counter passes, one
+# summary per workload under profiles/
+# ---------------------------------------------------------------------------
+COUNTER_PASSES = {
+    # MFMA pipe busy cycles / co-issue / instruction mix (8 SQ + 1 GRBM counters)
+    "mfma": "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+            "SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    # MFMA operations executed per type (x512 = ops) and LDS use
+    "mops": "SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+    # HBM-side bytes (in KiB per dispatch), one TCC-heavy counter per pass
+    "fetch": "FETCH_SIZE GRBM_GUI_ACTIVE",
+    "write": "WRITE_SIZE GRBM_GUI_ACTIVE",
+}
+SIMD_NUM = 1024   # 256 CUs x 4 SIMDs
+XCD_NUM = 8       # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs
+
+# workload -> summary file, kernel-name patterns of its hot kernels, sources
+COUNTER_WORKLOADS = {
+    "c2": {"file": "counters_k_prefill_sage_varlen.md", "kernels": [r"k_prefill<128, 2, false, false>"],
+           "title": "int8-QK / fp16-PV varlen prefill (SageAttention workload: B=8, lengths U{512..4096} seed "
+                    "1002, causal, Hq=32, Hkv=8, D=128; 16-bit Q quantized in the kernel)",
+           "sources": ("paged_kv_amd/csrc/prefill.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")},
+    "c5": {"file": "counters_k_prefill_fp8_long.md", "kernels": [r"k_prefill<128, 0, false, true>"],
+           "title": "fp8 prefill, QK^T summed exactly on f16 MFMAs (long workload: B=1, S=32768, H=64, D=128, "
+                    "causal, after RoPE + paged append + fp8 quantization)",
+           "sources": ("paged_kv_amd/csrc/prefill.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")},
+    "c3": {"file": "counters_k_decode_paged_fp8.md", "kernels": [r"k_decode_split<128>", r"k_decode_merge<128>"],
+           "title": "paged fp8 decode, split-KV + merge (B=64, kv lens U{1024..32768} seed 1003, page 16, "
+                    "Hq=32, Hkv=8, D=128)",
+           "sources": ("paged_kv_amd/csrc/decode.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")},
+    "c4": {"file": "counters_k_mla_sparse_decode.md", "kernels": [r"k_mla_split", r"k_mla_merge"],
+           "title": "sparse MLA-absorb decode (B=32, 128 heads, 2048 selected 656-byte rows per query, "
+                    "65536-token caches in 64-token blocks)",
+           "sources": ("paged_kv_amd/csrc/mla.hip", "paged_kv_amd/csrc/mla.h", "paged_kv_amd/csrc/kcommon.h",
+                       "paged_kv_amd/csrc/launch.h")},
+}
+
+
+def kernel_source_hash(sources) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_probe():
-    """One calibration copy of CALIB_BYTES and one headline prefill launch
-    (run under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)."""
+def _config2_flops():
+    import gen
+    return 4.0 * 128 * 32 * causal_pairs(gen.configs.config2_lengths())
+
+
+def _algorithmic(wl):
+    """(unit, algorithmic work of one launch of the workload's hot kernels)."""
+    import gen
+    if wl == "c2":
+        return "flop", _config2_flops()
+    if wl == "c5":
+        return "flop", 4.0 * 128 * 64 * causal_pairs([32768])
+    if wl == "c3":
+        lens = gen.configs.config3_lengths().astype(np.int64)
+        npages = (lens + 15) // 16
+        return "byte", float(lens.sum() * 8 * 128 * 2 + 64 * 32 * 128 * 2 * 2 + npages.sum() * 4 + 65 * 4 * 2)
+    if wl == "c4":
+        return "byte", float(C4_BYTES)
+    raise ValueError(wl)
+
+
+C4_BYTES = 32 * 2048 * 656 + 32 * 128 * 576 * 2 + 32 * 128 * 512 * 2 + 32 * 2048 * 4 + 32 * 1024 * 4
+
+
+def counter_probe(wl):
+    """One calibration copy of CALIB_BYTES, then one launch of workload wl's
+    hot kernels after its set-up (run under rocprofv3 --pmc, one pass per
+    counter group)."""
     import torch
     import gen
-    from paged_kv_amd.pipeline import SagePrefill
     from tests.parity import to_dev
     src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
-    x = gen.config2()
-    p = SagePrefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
-                    int(x["seqlens"].max()), x["sm_scale"], causal=True)
-    p.quantize()
     torch.cuda.synchronize()
-    p.attend()
+    if wl == "c2":
+        from paged_kv_amd.pipeline import SagePrefill
+        x = gen.config2()
+        p = SagePrefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
+                        int(x["seqlens"].max()), x["sm_scale"], causal=True)
+        p.quantize()
+        torch.cuda.synchronize()
+        p.attend()
+    elif wl == "c5":
+        from paged_kv_amd.pipeline import AppendRopeFp8Prefill
+        x = gen.config5()
+        kc = torch.zeros((x["num_pages"], x["page_size"], 64, 128), dtype=torch.bfloat16, device="cuda")
+        p = AppendRopeFp8Prefill(to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["cu_seqlens"]),
+                                 to_dev(x["kv_len_before"]), 32768, to_dev(x["rope_cos_sin"]), kc, torch.zeros_like(kc),
+                                 to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]), x["page_size"], x["sm_scale"])
+        p.append()
+        p.prefill.quantize()
+        torch.cuda.synchronize()
+        p.prefill.attend()
+    elif wl == "c3":
+        from paged_kv_amd.pipeline import PagedDecode
+        x = gen.config3()
+        p = PagedDecode(to_dev(x["q"]), to_dev(x["k_cache"]), to_dev(x["v_cache"]), to_dev(x["k_scale"]),
+                        to_dev(x["v_scale"]), to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]),
+                        to_dev(x["kv_last_page_len"]), x["max_kv_len"], x["sm_scale"])
+        torch.cuda.synchronize()
+        p.run()
+    elif wl == "c4":
+        from paged_kv_amd.pipeline import SparseMlaDecode
+        x = gen.config4()
+        p = SparseMlaDecode(to_dev(x["q"]), to_dev(x["kv_cache"]), to_dev(x["block_table"]),
+                            to_dev(x["kv_lens"]), to_dev(x["sparse_indices"]), x["sm_scale"])
+        torch.cuda.synchronize()
+        p.run()
+    else:
+        raise SystemExit(f"unknown workload {wl}")
     torch.cuda.synchronize()
-    log("[bench] traffic probe done")
+    log(f"[bench] counter probe {wl} done")
 
 
 def _counter_rows(d):
@@ -451,67 +574,126 @@ def _counter_rows(d):
     return list(csv.DictReader(open(f[0])))
 
 
-def summarize_traffic(fetch_dir, write_dir, fetch_cmd, write_cmd):
-    """Turn the two counter runs into profiles/traffic_k_prefill_sage_varlen.md."""
-    out = {}
-    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
-        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        pf = [float(r["Counter_Value"]) for r in rows if "k_prefill" in r["Kernel_Name"]]
-        if not copies or len(pf) != 1:
-            raise SystemExit(f"{name}: expected copy dispatches and one k_prefill dispatch, got {len(copies)}, {len(pf)}")
-        calib = max(copies)  # KiB for the CALIB_BYTES copy
-        factor = (CALIB_BYTES / 1024.0) / calib
-        out[name] = {"kernel_kib": pf[0], "copy_kib": calib, "factor": factor, "bytes": pf[0] * factor * 1024.0}
-    traffic = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
-    import gen
-    lens = gen.configs.config2_lengths()
-    t, spad = int(lens.sum()), (int(lens.max()) + 127) // 128 * 128
-    unique = t * 32 * 128 * 2 + t * 8 * 128 + len(lens) * 8 * 128 * spad * 2 + t * 32 * 128 * 2 \
-        + len(lens) * 8 * (spad // 128) * 4
-    h = kernel_source_hash()
-    lines = [
-        "# HBM-side traffic of one k_prefill launch (sage varlen workload: fp16 Q quantized to int8 in",
-        "# the kernel, int8 K, fp16 V^T, fp16 O)",
-        "",
-        "Workload: B=8, lengths U{512..4096} (seed 1002), causal, Hq=32, Hkv=8, D=128; one launch of",
-        "`attn_prefill_varlen` (INT8_PER_BLOCK_RAW_Q) after `attn_quant_qk` (K) and",
-        "`attn_quant_v_permute` (V) (bench.py --traffic-probe).",
-        "",
-        f"Unique bytes the launch must move: {unique:.4g} (fp16 Q + int8 K + fp16 V^T with its padding",
-        "+ fp16 O + scales), against the measured total below.",
-        "",
-        "Commands (from the repository root on the GPU host, `cd /tmp && export TMPDIR=/tmp` first):",
-        "",
-        f"    {fetch_cmd}",
-        f"    {write_cmd}",
-        "",
-        "Calibration: a device-to-device copy of 256 MiB (__amd_rocclr_copyBuffer) moves 262144 KiB each way;",
-        "each counter is scaled by 262144 / (its reading for that copy).",
-        "",
-        "| counter | k_prefill (KiB) | 256 MiB copy (KiB) | factor | k_prefill bytes |",
-        "|---|---|---|---|---|",
-    ]
-    for name in ("FETCH_SIZE", "WRITE_SIZE"):
-        o = out[name]
-        lines.append(f"| {name} | {o['kernel_kib']:.0f} | {o['copy_kib']:.0f} | {o['factor']:.4f} | {o['bytes']:.4g} |")
-    lines += ["", f"traffic_bytes_per_launch: {traffic:.6g}", f"kernel_source_hash: {h}", ""]
-    with open(TRAFFIC_FILE, "w") as fh:
+def _pass_values(d, patterns):
+    """Counter values of one pass: (sum over the workload's hot-kernel
+    dispatches, per-kernel values, calibration copy values, summed dispatch
+    durations in ns)."""
+    rows = _counter_rows(d)
+    hot, per, copy = {}, {}, {}
+    dur = {}
+    for r in rows:
+        name, cn, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+        if "copyBuffer" in name:
+            copy[cn] = max(copy.get(cn, 0.0), v)
+            continue
+        for pat in patterns:
+            if pat in name:
+                per.setdefault(pat, {})[cn] = v          # the last dispatch of that kernel
+                dur[pat] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for pat, vals in per.items():
+        for cn, v in vals.items():
+            hot[cn] = hot.get(cn, 0.0) + v
+    missing = [p for p in patterns if p not in per]
+    if missing:
+        raise SystemExit(f"{d}: no dispatch of {missing}")
+    return hot, per, copy, float(sum(dur.values()))
+
+
+def summarize_counters(wl, run_dir):
+    """Write profiles/<file> for workload wl from the passes under run_dir
+    (one subdirectory per pass, named as in COUNTER_PASSES, and cmds.txt with
+    the commands that made them)."""
+    cfg = COUNTER_WORKLOADS[wl]
+    pats = cfg["kernels"]
+    cmds = open(os.path.join(run_dir, "cmds.txt")).read().strip().splitlines()
+    vals, per_kernel, copies, durs = {}, {}, {}, {}
+    for pname in COUNTER_PASSES:
+        d = os.path.join(run_dir, pname)
+        if not os.path.isdir(d):
+            continue
+        hot, per, copy, dur = _pass_values(d, pats)
+        vals.update({k: v for k, v in hot.items() if k != "GRBM_GUI_ACTIVE"})
+        vals[f"GRBM_GUI_ACTIVE[{pname}]"] = hot.get("GRBM_GUI_ACTIVE", 0.0)
+        for pat, pv in per.items():
+            per_kernel.setdefault(pat, {}).update({k: v for k, v in pv.items() if k != "GRBM_GUI_ACTIVE"})
+        copies[pname] = copy
+        durs[pname] = dur
+    unit, work = _algorithmic(wl)
+    lines = [f"# rocprofv3 counters: {cfg['title']}", "",
+             "Kernels: " + ", ".join(f"`{p}`" for p in pats) + " (one launch each, counters summed over them).", "",
+             "Commands (repository root on the GPU host; `cd /tmp && export TMPDIR=/tmp` first, R = the root):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", "| counter | " + " | ".join(f"`{p}`" for p in pats) + " | total |",
+              "|---|" + "---|" * (len(pats) + 1)]
+    for cn in sorted(k for k in vals if not k.startswith("GRBM")):
+        lines.append(f"| {cn} | " + " | ".join(f"{per_kernel[p].get(cn, float('nan')):.6g}" for p in pats)
+                     + f" | {vals[cn]:.6g} |")
+    for k in sorted(k for k in vals if k.startswith("GRBM")):
+        lines.append(f"| {k} | | {vals[k]:.6g} |")
+    derived = {}
+    lines += ["", "Derived (per launch):", ""]
+    if "mfma" in durs:
+        grbm = vals["GRBM_GUI_ACTIVE[mfma]"] / XCD_NUM          # cycles of one XCD
+        util = 100.0 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm * SIMD_NUM)
+        coexec = 100.0 * vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(vals["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0)
+        derived["mfma_util_pct"] = util
+        lines += [f"- MFMA pipe busy (rocprof's MfmaUtil: sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCD "
+                  f"x {SIMD_NUM} SIMDs)): **{util:.1f}%**",
+                  f"- cycles with a VALU instruction issued beside a busy MFMA pipe: {coexec:.1f}% of the MFMA busy cycles",
+                  f"- VALU instructions per MFMA instruction: {vals['SQ_INSTS_VALU'] / max(vals['SQ_INSTS_MFMA'], 1):.2f} "
+                  f"(transcendental fp32: {vals['SQ_INSTS_VALU_TRANS_F32'] / max(vals['SQ_INSTS_MFMA'], 1):.2f})",
+                  f"- engine clock under the kernel: {grbm / max(durs['mfma'], 1.0):.3f} GHz (GRBM_GUI_ACTIVE of one XCD "
+                  f"/ dispatch time {durs['mfma'] / 1e3:.1f} us)"]
+    if "mops" in durs:
+        ops = {t: 512.0 * vals.get(f"SQ_INSTS_VALU_MFMA_MOPS_{t}", 0.0) for t in ("I8", "F8", "F16", "BF16")}
+        tot = sum(ops.values())
+        derived["mfma_ops"] = tot
+        lines += ["- MFMA operations executed: " + ", ".join(f"{t} {v:.4g}" for t, v in ops.items() if v)
+                  + f"; total {tot:.4g}"]
+        if unit == "flop":
+            lines += [f"- algorithmic flop of the launch {work:.4g}: executed / algorithmic = {tot / work:.3f} "
+                      "(tiles crossing the causal diagonal or a sequence end are computed whole)"]
+    if "fetch" in durs and "write" in durs:
+        fcal = (CALIB_BYTES / 1024.0) / copies["fetch"]["FETCH_SIZE"]
+        wcal = (CALIB_BYTES / 1024.0) / copies["write"]["WRITE_SIZE"]
+        fb = vals["FETCH_SIZE"] * fcal * 1024.0
+        wb = vals["WRITE_SIZE"] * wcal * 1024.0
+        derived["traffic"] = fb + wb
+        lines += [f"- HBM-side traffic: FETCH_SIZE {vals['FETCH_SIZE']:.0f} KiB x {fcal:.4f} + WRITE_SIZE "
+                  f"{vals['WRITE_SIZE']:.0f} KiB x {wcal:.4f} = {fb:.4g} + {wb:.4g} = **{fb + wb:.4g} bytes** "
+                  f"(factors: {CALIB_BYTES >> 20} MiB device copy, {CALIB_BYTES / 1024:.0f} KiB each way, read "
+                  f"{copies['fetch']['FETCH_SIZE']:.0f} KiB fetched and {copies['write']['WRITE_SIZE']:.0f} KiB written)"]
+        if unit == "byte":
+            lines += [f"- algorithmic bytes {work:.4g}: traffic / algorithmic = {(fb + wb) / work:.3f}",
+                      f"- at the dispatch time of the fetch pass ({durs['fetch'] / 1e3:.1f} us, caches as the probe left "
+                      f"them): {work / durs['fetch']:.1f} GB/s algorithmic, {(fb + wb) / durs['fetch']:.1f} GB/s measured"]
+    lines += ["", "Machine-readable:", ""]
+    if "traffic" in derived:
+        lines.append(f"traffic_bytes_per_launch: {derived['traffic']:.6g}")
+    if "mfma_util_pct" in derived:
+        lines.append(f"mfma_util_pct: {derived['mfma_util_pct']:.4g}")
+    if "mfma_ops" in derived:
+        lines.append(f"mfma_ops_per_launch: {derived['mfma_ops']:.6g}")
+    lines += [f"kernel_source_hash: {kernel_source_hash(cfg['sources'])}", ""]
+    out = os.path.join(ROOT, "profiles", cfg["file"])
+    with open(out, "w") as fh:
         fh.write("\n".join(lines))
-    print(json.dumps({"traffic_bytes": traffic, "hash": h, **out}))
+    print(json.dumps({"file": out, **derived}))
 
 
-def stored_traffic():
-    """Bytes per launch from the committed counter summary, or None when the
-    kernel sources changed since the counters were taken."""
+def stored_counters(wl):
+    """Machine-readable figures of workload wl's counter summary, or {} when
+    the kernel sources changed since the counters were taken."""
+    cfg = COUNTER_WORKLOADS[wl]
     try:
-        txt = open(TRAFFIC_FILE).read()
+        txt = open(os.path.join(ROOT, "profiles", cfg["file"])).read()
     except OSError:
-        return None
-    vals = dict(l.split(": ", 1) for l in txt.splitlines() if l.startswith(("traffic_bytes_per_launch", "kernel_source_hash")))
-    if vals.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return float(vals["traffic_bytes_per_launch"])
+        return {}
+    vals = dict(l.split(": ", 1) for l in txt.splitlines()
+                if l.startswith(("traffic_bytes_per_launch", "kernel_source_hash", "mfma_util_pct", "mfma_ops_per_launch")))
+    if vals.get("kernel_source_hash") != kernel_source_hash(cfg["sources"]):
+        return {}
+    return {k: float(v) for k, v in vals.items() if k != "kernel_source_hash"}
 
 
 def cpu_baseline(x, budget_s=12.0):
@@ -557,13 +739,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--extra", default="c3,c5,c4,paged", help="comma list of extra workloads (c3,c4,c5,paged) or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="run the calibration copy and one prefill launch (for rocprofv3 --pmc)")
-    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "FETCH_CMD", "WRITE_CMD"),
-                    help="write the traffic summary under profiles/ from two counter runs")
+    ap.add_argument("--counter-probe", choices=sorted(COUNTER_WORKLOADS),
+                    help="run the calibration copy and one launch of a workload's hot kernels (for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("WORKLOAD", "RUN_DIR"),
+                    help="write profiles/counters_*.md from the counter passes under RUN_DIR")
+    ap.add_argument("--list-counter-passes", action="store_true",
+                    help="print the counter groups of the passes, one per line (name: counters)")
     a = ap.parse_args()
-    if a.summarize_traffic:
-        summarize_traffic(*a.summarize_traffic)
+    if a.summarize_counters:
+        summarize_counters(*a.summarize_counters)
+        return
+    if a.list_counter_passes:
+        for k, v in COUNTER_PASSES.items():
+            print(f"{k}: {v}")
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -574,8 +762,8 @@ def main():
     torch.cuda.set_device(0)
     import paged_kv_amd
     paged_kv_amd.lib()
-    if a.traffic_probe:
-        traffic_probe()
+    if a.counter_probe:
+        counter_probe(a.counter_probe)
         return
 
     log("[bench] config2 (headline)")
@@ -619,7 +807,8 @@ def main():
                    "step_flop": r2["flops"]},
         "pct_fp8_peak": 100 * value / PEAK_FP8,
         "roofline": {"bound": "mfma", "achieved": k_tflops, "peak": peak_mixed, "unit": "TFLOP/s",
-                     "frac": k_tflops / peak_mixed, "traffic": stored_traffic(),
+                     "frac": k_tflops / peak_mixed, "traffic": stored_counters("c2").get("traffic_bytes_per_launch"),
+                     "mfma_util_pct": stored_counters("c2").get("mfma_util_pct"),
                      "kernel": "k_prefill<128, int8 QK, fp16 V>",
                      "per_launch_flop": r2["flops"], "avg_launch_ms": r2["kernel_ms"]},
         "cpu_baseline": cpu,
