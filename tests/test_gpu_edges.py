@@ -198,11 +198,14 @@ def test_decode_head_dim_64_groups(hq, hkv):
 def _compare_wide_range(got, want_r, want_ex, label):
     """Outputs whose magnitude spans many decades (tile scales up to 1e3 make
     |O| up to ~1e5, where one bf16 ulp is 512): every element within
-    max(2e-2, 1 bf16 ulp at the exact value) and the mean error relative to
-    max(1, |O|) at most 2e-3.  (The absolute rule presumes |O| of order 1.)"""
+    max(2e-2, 2 bf16 ulps at the exact value) and the mean error relative to
+    max(1, |O|) at most 2e-3.  (The absolute rule presumes |O| of order 1.)
+    Two ulps: before the output's own rounding, a value passes two bf16
+    roundings of at most half an ulp each -- P * tile scale as the PV operand
+    and the split's partial O -- so 1.5 ulps of error can round to 2."""
     from tests.parity import ulp_at
     err = np.abs(np.asarray(got, np.float64) - want_r)
-    bound = np.maximum(2e-2, ulp_at(want_ex, "bf16") * (1 + 1e-12))
+    bound = np.maximum(2e-2, 2 * ulp_at(want_ex, "bf16") * (1 + 1e-12))
     assert np.all(err <= bound), f"{label}: worst err / bound {(err / bound).max():.3g}"
     rel = float((err / np.maximum(1.0, np.abs(want_ex))).mean())
     assert rel <= 2e-3, f"{label}: mean relative err {rel:.3g}"
