@@ -10,9 +10,11 @@ TFLOP/s (4 * D * H_q * sum over sequences of L(L+1)/2).
 
 Also reported (``extra``): the paged fp8 decode (GB/s of K/V bytes), the
 long fp8 prefill with RoPE + paged append (TFLOP/s), the sparse MLA decode
-(GB/s) and a chunked prefill against a paged bf16 cache (TFLOP/s of the
-prefill alone and of page gather + quantization + prefill), each timed on
-its own, each with the oracle timed beside it on a bounded sample.
+(GB/s), a chunked prefill against a paged bf16 cache (TFLOP/s of the
+prefill alone and of page gather + quantization + prefill) and the same
+chunks against a paged fp8 cache read inside the prefill kernel (Q
+quantization + prefill), each timed on its own, the first four with the
+oracle timed beside them on a bounded sample.
 
 ``roofline``: the prefill kernel alone, timed with HIP events on the stream
 it is launched on, against the MFMA peak of its two contractions (int8 QK at
@@ -321,6 +323,37 @@ def bench_paged_prefill(iters, cpu=False):
     if cpu:
         r["cpu_oracle"] = oracle_paged_prefill(x)
     return r
+
+
+def bench_paged_prefill_fp8(iters):
+    """Chunked prefill against a paged fp8 cache, the pages read inside the
+    kernel: fp8 per-head Q quantization + the paged prefill.  The same
+    lengths, heads and page size as the bf16-cache flow; Q is that flow's
+    bf16 chunk."""
+    import torch
+    import gen
+    from paged_kv_amd.pipeline import PagedPrefillFp8
+    from tests.parity import to_dev
+    x = gen.paged_prefill_fp8_workload()
+    qb = gen.paged_prefill_workload()["q"]
+    assert qb.shape == x["q"].shape
+    p = PagedPrefillFp8(to_dev(qb), to_dev(x["k_cache"]), to_dev(x["v_cache"]), to_dev(x["k_scale"]),
+                        to_dev(x["v_scale"]), to_dev(x["kv_indptr"]), to_dev(x["kv_indices"]),
+                        to_dev(x["kv_last_page_len"]), to_dev(x["cu_q"]), x["max_q"], x["max_kv_len"],
+                        x["sm_scale"], causal=True)
+    p.run()
+    torch.cuda.synchronize()
+    lq, lk = x["q_lens"].astype(np.int64), x["kv_lens"].astype(np.int64)
+    pairs = float(np.sum(lq * (lk - lq) + lq * (lq + 1) // 2))
+    flops = 4.0 * 128 * 32 * pairs
+    settle(p.attend)
+    kms = time_events(p.attend, iters)
+    pipe = time_events(p.run, max(2, iters // 2))
+    med = float(np.median(kms))
+    return {"prefill_ms": med, "prefill_TFLOPS": flops / (med * 1e-3) / 1e12,
+            "pct_fp8_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_FP8,
+            "pipeline_ms": float(np.median(pipe)),
+            "pipeline_TFLOPS": flops / (np.median(pipe) * 1e-3) / 1e12}
 
 
 def oracle_paged_prefill(x, budget_s=4.0):
@@ -737,7 +770,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--extra", default="c3,c5,c4,paged", help="comma list of extra workloads (c3,c4,c5,paged) or ''")
+    ap.add_argument("--extra", default="c3,c5,c4,paged,paged_fp8",
+                    help="comma list of extra workloads (c3,c4,c5,paged,paged_fp8) or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counter-probe", choices=sorted(COUNTER_WORKLOADS),
                     help="run the calibration copy and one launch of a workload's hot kernels (for rocprofv3 --pmc)")
@@ -781,14 +815,15 @@ def main():
                          "prefill_kernel_TFLOPS": k_tflops, "pct_fp8_peak_step": 100 * value / PEAK_FP8,
                          "pct_fp8_peak_kernel": 100 * k_tflops / PEAK_FP8}}
     for name, fn, it in (("c3", bench_config3, 20), ("c5", bench_config5, 5), ("c4", bench_config4, 30),
-                         ("paged", bench_paged_prefill, 10)):
+                         ("paged", bench_paged_prefill, 10), ("paged_fp8", bench_paged_prefill_fp8, 10)):
         if name not in a.extra.split(","):
             continue
         log(f"[bench] {name}")
         try:
+            kw = {} if name == "paged_fp8" else {"cpu": not a.no_cpu_baseline}
             extra[{"c3": "config3_decode", "c5": "config5_long_prefill", "c4": "config4_sparse_mla",
-                   "paged": "chunked_prefill_paged"}[name]] = \
-                fn(it, cpu=not a.no_cpu_baseline)
+                   "paged": "chunked_prefill_paged", "paged_fp8": "chunked_prefill_paged_fp8"}[name]] = \
+                fn(it, **kw)
         except Exception as ex:  # report, keep the headline line
             extra[name] = {"error": f"{type(ex).__name__}: {ex}"}
         torch.cuda.empty_cache()

@@ -25,7 +25,7 @@ import numpy as np
 
 __all__ = [
     "seed_for", "bf16_bits", "fp8_lut_codes",
-    "prefill_fp8_inputs", "config1",
+    "prefill_fp8_inputs", "config1", "paged_prefill_fp8_inputs", "paged_prefill_fp8_workload",
     "sage_inputs", "config2",
     "paged_decode_inputs", "config3",
     "sparse_mla_inputs", "config4",
@@ -436,6 +436,38 @@ def paged_prefill_inputs(seed: int, kv_lens, q_lens, hq: int, hkv: int, d: int,
         "num_pages": pool, "page_size": page_size, "hq": hq, "hkv": hkv, "d": d,
         "max_q": int(q_lens.max()) if b else 0, "max_k": int(kv_lens.max()) if b else 0,
     }
+
+
+def paged_prefill_fp8_inputs(seed: int, kv_lens, q_lens, hq: int, hkv: int, d: int,
+                             page_size: int = 64, spare_frac: float = 0.05) -> dict:
+    """A prefill chunk (the last q_lens[b] of kv_lens[b] positions of
+    sequence b) against fp8 e4m3fn K/V page pools: the caches, page
+    permutation, NaN spare pages and NaN stale slots of paged_decode_inputs,
+    plus fp8 query codes [sum q_lens, hq, d] (the same normal-like code
+    distribution) with positive per-head descales, and cu_q."""
+    kv_lens = np.asarray(kv_lens, np.int64)
+    q_lens = np.asarray(q_lens, np.int64)
+    assert kv_lens.shape == q_lens.shape and np.all(q_lens <= kv_lens)
+    x = paged_decode_inputs(seed, kv_lens, hq, hkv, d, page_size, spare_frac)
+    rng = np.random.default_rng(seed + 7919)
+    del x["q"]
+    x["q"] = fp8_lut_codes(rng, (int(q_lens.sum()), hq, d))
+    x["q_scale"] = (rng.uniform(0.8, 1.2, size=hq) * 4.5 / 448.0).astype(np.float32)
+    x["q_lens"] = q_lens.astype(np.int32)
+    x["cu_q"] = _cu(q_lens)
+    x["max_q"] = int(q_lens.max()) if q_lens.size else 0
+    return x
+
+
+def paged_prefill_fp8_workload() -> dict:
+    """The chunked-prefill workload (B=4 sequences of kv_len U{8192..24576},
+    seeded, each with a 2048-token chunk at its end; 32 q / 8 kv heads,
+    D=128, page size 64, causal) over an fp8 e4m3fn cache with per-head
+    descales."""
+    kv = paged_prefill_workload_lengths()
+    x = paged_prefill_fp8_inputs(seed_for(6) + 2, kv, np.full(kv.size, 2048), 32, 8, 128, 64)
+    x.update(sm_scale=1.0 / math.sqrt(128.0), name="chunked_prefill_paged_fp8")
+    return x
 
 
 def paged_prefill_workload_lengths(seed: int = None, batch: int = 4):

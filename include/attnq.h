@@ -273,6 +273,42 @@ int attn_gather_paged_kv(const void* cache, int elem_bytes, const int32_t* kv_in
                          hipStream_t stream);
 
 /*
+ * attn_prefill_paged -- a prefill chunk attending to a paged fp8 KV cache,
+ * the pages read inside the attention kernel (FlashInfer
+ * BatchPrefillWithPagedKVCacheRun over paged_kv_indptr / paged_kv_indices /
+ * paged_kv_last_page_len; aiter's flash_attn_with_kvcache with an fp8 cache,
+ * a page table and descales).
+ *   q fp8 e4m3fn codes [total_q, num_q_heads, head_dim] with q_scale fp32 [Hq]
+ *     (attn_quant_qk FP8_PER_HEAD); scale_mode FP8_PER_HEAD (QK^T summed
+ *     exactly, as in attn_prefill_varlen) or FP8_PER_HEAD_MFMA8.
+ *   k_cache / v_cache fp8 e4m3fn [num_pages, page_size, num_kv_heads, head_dim]
+ *     (NHD), k_scale / v_scale fp32 [Hkv]: the cache attn_decode_paged reads.
+ *   kv_indptr [batch+1], kv_indices, kv_last_page_len [batch]: sequence b's
+ *     keys are kv_len[b] = (kv_indptr[b+1]-kv_indptr[b]-1)*page_size +
+ *     kv_last_page_len[b] tokens (0 without a page), token t in page
+ *     kv_indices[kv_indptr[b] + t/page_size], slot t % page_size.  Page ids
+ *     outside [0, num_pages) are clamped into it.  Slots past kv_len in the
+ *     last page may hold anything (NaN codes included): they are not read
+ *     into the result.
+ *   cu_seqlens_q [batch+1]: the chunk's queries of sequence b, the last
+ *     L_q of its kv_len positions (causal: query i sees key j iff
+ *     j <= i + kv_len - L_q).
+ *   max_seqlen_q, max_kv_len: host upper bounds of L_q and kv_len.
+ *   logit, masking, sm_scale (NaN: 1/sqrt(head_dim)), o [total_q, Hq, D]
+ *   (BF16 or FP16) and lse (optional fp32 [Hq, total_q]) as attn_prefill_varlen.
+ *   Supported: head_dim 64 or 128, page_size a multiple of 16 in [16, 1024],
+ *   num_pages * page_size * num_kv_heads * head_dim < 2^31 bytes, else
+ *   ATTNQ_EUNSUPPORTED.
+ */
+int attn_prefill_paged(const void* q, const float* q_scale, int scale_mode, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_last_page_len, const int32_t* cu_seqlens_q, int batch,
+                       int num_pages, int page_size, int max_seqlen_q, int max_kv_len, int total_q,
+                       int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, int causal,
+                       void* o, int o_dtype, float* lse, hipStream_t stream);
+
+/*
  * attn_decode_paged -- one query token per sequence against a paged fp8 cache,
  * split over KV chunks and merged by log-sum-exp (FlashInfer
  * BatchDecodeWithPagedKVCachePlan/Run; aiter's paged fp8 flash_attn_with_kvcache).

@@ -29,6 +29,8 @@ Functions:
                      block_table, sparse_indices, sparse_block_size, sparse_mode
                      0 or 3; sparse_mla_tokens states which tokens a query
                      row uses
+  prefill_paged      a prefill chunk over a paged fp8 cache (FlashInfer's paged
+                     prefill run; aiter's flash_attn_with_kvcache, fp8 cache)
   ragged_from_pages  a paged cache read back into the ragged [T, H, D] layout
   dequant_*          code * scale for fp8 per head / per channel and int8 per block
   lse_merge          combination of split partials (O_c, lse_c)
@@ -236,6 +238,27 @@ def decode_paged(q_bits, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indic
             o_ex[b, h], lse[b, h] = o[0], l[0]
     r, st = _round_out(o_ex, "bf16")
     return {"o_exact": o_ex, "o": r, "o_store": st, "lse": lse.astype(np.float32)}
+
+
+def prefill_paged(q_codes, q_scale, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices,
+                  kv_last_page_len, cu_q, sm_scale, causal, out_dtype="bf16", rows=None):
+    """A prefill chunk against a paged fp8 cache (FlashInfer's prefill over
+    paged_kv_indptr / paged_kv_indices / paged_kv_last_page_len; aiter's
+    flash_attn_with_kvcache with an fp8 e4m3 cache, a page table and
+    descales): q_codes [Tq, Hq, D] e4m3fn with q_scale [Hq]; caches
+    [P, page_size, Hkv, D] e4m3fn with k_scale / v_scale [Hkv].  Sequence b's
+    keys are its kv_len[b] cached tokens (page kv_indices[kv_indptr[b] +
+    t // page_size], slot t % page_size); its queries, rows cu_q[b] ..
+    cu_q[b+1], are the last L_q of those positions (the bottom-right causal
+    alignment of prefill_varlen).  The pages read into the ragged layout,
+    dequantized, then prefill_varlen (same returns, ``rows`` as there)."""
+    ps = k_cache.shape[1]
+    lens = paged_kv_len(kv_indptr, kv_last_page_len, ps)
+    cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    kd = dequant_fp8_per_head(ragged_from_pages(k_cache, kv_indptr, kv_indices, kv_last_page_len, cu_k), k_scale)
+    vd = dequant_fp8_per_head(ragged_from_pages(v_cache, kv_indptr, kv_indices, kv_last_page_len, cu_k), v_scale)
+    qd = dequant_fp8_per_head(q_codes, q_scale)
+    return prefill_varlen(qd, kd, vd, cu_q, cu_k, sm_scale, causal, out_dtype, rows)
 
 
 # ---------------------------------------------------------------------------

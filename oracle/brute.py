@@ -183,6 +183,37 @@ def decode_paged(q_bits, k_cache, v_cache, k_scale, v_scale, indptr, indices, la
     return o, lse
 
 
+def prefill_paged(q_codes, q_scale, k_cache, v_cache, k_scale, v_scale, indptr, indices, last, cu_q,
+                  scale, causal):
+    """Scalar page walk of a prefill chunk over fp8 pages: query i of
+    sequence b (of L_q) sits at position i + n - L_q of its n cached tokens."""
+    tq, hq, d = q_codes.shape
+    ps, hkv = k_cache.shape[1], k_cache.shape[2]
+    o = np.zeros((tq, hq, d))
+    lse = np.full((hq, tq), -np.inf)
+    for b in range(len(cu_q) - 1):
+        npg = int(indptr[b + 1] - indptr[b])
+        n = 0 if npg == 0 else (npg - 1) * ps + int(last[b])
+        lq = int(cu_q[b + 1] - cu_q[b])
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for i in range(lq):
+                keys, vals = [], []
+                for t in range(n):
+                    if causal and t > i + n - lq:
+                        continue
+                    page = int(indices[int(indptr[b]) + t // ps])
+                    slot = t % ps
+                    keys.append([e4m3fn_value(int(k_cache[page, slot, g, c])) * float(k_scale[g]) for c in range(d)])
+                    vals.append([e4m3fn_value(int(v_cache[page, slot, g, c])) * float(v_scale[g]) for c in range(d)])
+                if not keys:
+                    continue
+                r = int(cu_q[b]) + i
+                q = [e4m3fn_value(int(q_codes[r, h, c])) * float(q_scale[h]) for c in range(d)]
+                o[r, h], lse[h, r] = attend_one(q, keys, vals, scale)
+    return o, lse
+
+
 def sparse_mla(q_bits, kv_cache, block_table, kv_lens, sparse_indices, scale, kv_dtype="int8",
                sparse_block_size=1, sparse_mode=0):
     """Scalar sparse MLA decode; rows parsed with struct.  Entry e >= 0 covers

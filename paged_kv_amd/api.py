@@ -18,7 +18,7 @@ __all__ = [
     "Q_INT8_PER_BLOCK_RAW_Q",
     "library_path", "lib", "abi_version",
     "attn_quant_qk", "attn_quant_v_permute", "attn_append_kv_rope", "attn_prefill_varlen",
-    "attn_smooth_quant_k", "attn_gather_paged_kv", "attn_decode_paged_workspace_size",
+    "attn_smooth_quant_k", "attn_gather_paged_kv", "attn_prefill_paged", "attn_decode_paged_workspace_size",
     "attn_decode_paged", "attn_decode_paged_noalloc",
     "attn_sparse_mla_decode_workspace_size", "attn_sparse_mla_decode", "attn_quant_kv",
     "SYMBOLS",
@@ -46,6 +46,8 @@ SYMBOLS = {
                                  _I, _I, _I, _I, _F, _I, _P, _I, _P, _P]),
     "attn_smooth_quant_k": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "attn_gather_paged_kv": (_I, [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "attn_prefill_paged": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                _I, _F, _I, _P, _I, _P, _P]),
     "attn_decode_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                _P, _Z, _P, _P, _P]),
@@ -173,6 +175,19 @@ def attn_gather_paged_kv(cache, elem_bytes, kv_indptr, kv_indices, kv_last_page_
                                       _ptr(kv_last_page_len), _ptr(cu_seqlens_k), batch,
                                       max_seqlen_k, num_pages, page_size, num_kv_heads, head_dim,
                                       _ptr(out), s), "attn_gather_paged_kv")
+
+
+def attn_prefill_paged(q, q_scale, scale_mode, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices,
+                       kv_last_page_len, cu_seqlens_q, batch, num_pages, page_size, max_seqlen_q, max_kv_len,
+                       total_q, num_q_heads, num_kv_heads, head_dim, sm_scale, causal, o, o_dtype, lse=None,
+                       stream=None):
+    s = _stream(stream, q, o)
+    _check(lib().attn_prefill_paged(_ptr(q), _ptr(q_scale), scale_mode, _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(k_scale), _ptr(v_scale), _ptr(kv_indptr), _ptr(kv_indices),
+                                    _ptr(kv_last_page_len), _ptr(cu_seqlens_q), batch, num_pages, page_size,
+                                    max_seqlen_q, max_kv_len, total_q, num_q_heads, num_kv_heads, head_dim,
+                                    float(sm_scale), int(causal), _ptr(o), o_dtype, _ptr(lse), s),
+           "attn_prefill_paged")
 
 
 def attn_decode_paged_workspace_size(batch, num_q_heads, head_dim, max_kv_len, page_size) -> int:

@@ -304,6 +304,67 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v_perm, int qk
   return ok();
 }
 
+// ---------------------------------------------------------------- attn_prefill_paged
+int attn_prefill_paged(const void* q, const float* q_scale, int scale_mode, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_last_page_len, const int32_t* cu_seqlens_q, int batch,
+                       int num_pages, int page_size, int max_seqlen_q, int max_kv_len, int total_q,
+                       int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, int causal,
+                       void* o, int o_dtype, float* lse, hipStream_t stream) {
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0, ATTNQ_EINVAL,
+          "num_q_heads must be a positive multiple of num_kv_heads");
+  REQUIRE(scale_mode == ATTNQ_Q_FP8_PER_HEAD || scale_mode == ATTNQ_Q_FP8_PER_HEAD_MFMA8, ATTNQ_EUNSUPPORTED,
+          "scale_mode must be FP8_PER_HEAD or FP8_PER_HEAD_MFMA8");
+  REQUIRE(is16(o_dtype), ATTNQ_EUNSUPPORTED, "o_dtype must be BF16 or FP16");
+  REQUIRE(page_size >= 16 && page_size <= 1024 && page_size % 16 == 0, ATTNQ_EINVAL,
+          "page_size must be a multiple of 16 in [16, 1024] (got %d)", page_size);
+  REQUIRE(batch >= 0 && max_seqlen_q >= 0 && max_kv_len >= 0 && total_q >= 0, ATTNQ_EINVAL, "sizes must be >= 0");
+  REQUIRE(num_pages > 0, ATTNQ_EINVAL, "num_pages must be positive");
+  REQUIRE(max_seqlen_q <= 65535 * 128, ATTNQ_EINVAL, "max_seqlen_q too large");
+  // the cache is addressed with 32-bit byte offsets, lanes past a sequence's
+  // last key with offset 2^31
+  REQUIRE((long)num_pages * page_size * num_kv_heads * head_dim < (1L << 31), ATTNQ_EUNSUPPORTED,
+          "the cache (num_pages * page_size * num_kv_heads * head_dim bytes) must stay below 2 GiB");
+  REQUIRE(scale_ok(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite (or NaN for 1/sqrt(head_dim))");
+  sm_scale = scale_or_default(sm_scale, head_dim);
+  if (batch == 0 || total_q == 0) return ok();
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(q_scale, 4);
+  REQUIRE_PTR(k_cache, 16);
+  REQUIRE_PTR(v_cache, 16);
+  REQUIRE_PTR(k_scale, 4);
+  REQUIRE_PTR(v_scale, 4);
+  REQUIRE_PTR(kv_indptr, 4);
+  REQUIRE_PTR(kv_indices, 4);
+  REQUIRE_PTR(kv_last_page_len, 4);
+  REQUIRE_PTR(cu_seqlens_q, 4);
+  REQUIRE_PTR(o, 16);
+  REQUIRE_OPT_PTR(lse, 4);
+  attnq::PrefillArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.v_chan = 0;
+  a.cu_q = cu_seqlens_q; a.cu_k = nullptr;
+  a.kv_indptr = kv_indptr; a.kv_indices = kv_indices; a.kv_last = kv_last_page_len;
+  a.page_size = page_size; a.num_pages = num_pages;
+  a.o = o; a.lse = lse;
+  a.q_scale_out = nullptr;
+  a.batch = batch; a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.s_pad = 0;
+  a.nblk_q = (max_seqlen_q + 127) / 128;
+  a.nblk_k = (max_kv_len + 127) / 128;
+  a.total_q = total_q; a.total_k = 0;
+  a.causal = causal ? 1 : 0;
+  a.max_q = max_seqlen_q;
+  a.max_k = max_kv_len;
+  a.sm_scale_log2 = sm_scale * LOG2E;
+  const int q_mode = scale_mode == ATTNQ_Q_FP8_PER_HEAD_MFMA8 ? attnq::PF_Q_FP8_MFMA8 : attnq::PF_Q_FP8;
+  LAUNCHED(attnq::launch_prefill_paged(a, head_dim, q_mode, o_dtype == ATTNQ_BF16, max_seqlen_q, stream));
+  return ok();
+}
+
 // ---------------------------------------------------------------- attn_smooth_quant_k
 int attn_smooth_quant_k(const void* k, const int32_t* cu_seqlens, int batch, int max_seqlen,
                         int total_tokens, int num_kv_heads, int head_dim, int block_tokens,

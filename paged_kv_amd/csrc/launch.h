@@ -44,6 +44,12 @@ struct PrefillArgs {
   int tblk;               // query tiles per block of the workgroup order (set by launch_prefill)
   int v_chan;             // v_scale holds one descale per (sequence, kv head, channel)
   float sm_scale_log2;    // sm_scale * log2(e)
+  // paged form: k and v are fp8 caches [num_pages, page_size, hkv, D], each
+  // sequence's keys in the pages kv_indices[kv_indptr[b] .. kv_indptr[b+1])
+  const int32_t* kv_indptr = nullptr;
+  const int32_t* kv_indices = nullptr;
+  const int32_t* kv_last = nullptr;
+  int page_size = 0, num_pages = 0;
 };
 // Q/K forms of the prefill: fp8 codes with per-head descales (QK^T summed
 // exactly: codes widened to fp16, f16 MFMA); the same with the fp8 MFMA
@@ -55,6 +61,10 @@ enum { PF_Q_FP8 = 0, PF_Q_I8 = 1, PF_Q_RAW_F16 = 2, PF_Q_RAW_BF16 = 3, PF_Q_FP8_
 // q_mode: one of PF_Q_*; v_fp8: fp8 V (else fp16 V)
 bool launch_prefill(const PrefillArgs& a, int head_dim, int q_mode, bool v_fp8, bool o_bf16,
                     int max_seqlen_q, hipStream_t s);
+// the same over fp8 K/V pages (PrefillArgs' paged fields; q_mode PF_Q_FP8 or
+// PF_Q_FP8_MFMA8)
+bool launch_prefill_paged(const PrefillArgs& a, int head_dim, int q_mode, bool o_bf16, int max_seqlen_q,
+                          hipStream_t s);
 
 struct DecodeArgs {
   const void* q;           // bf16 [B, Hq, D]

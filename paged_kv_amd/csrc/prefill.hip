@@ -82,6 +82,8 @@ struct PfGeo {
   static constexpr int LDS = V_OFF + NV_ST * VBYTES;
   static ATTNQ_DEV int ksw(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
   static ATTNQ_DEV int vsw(int r) { return (r >> 1) & 7; }
+  // token-major fp16 V rows (paged form): D / 8 chunks per row
+  static ATTNQ_DEV int tsw(int r) { return r & (D / 8 - 1); }
 };
 
 ATTNQ_DEV __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, uint32_t bytes) {
@@ -144,6 +146,15 @@ ATTNQ_DEV void pf_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, co
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vdst + j * 1024), 16, vvo[j], v_soff, 0, 0);
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane
+// 4k + q names 4 consecutive 16-bit values of row k; lane n receives value n
+// of the 4 rows (column n of the 4 x 16 block).
+typedef __fp16 pf_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+ATTNQ_DEV u32x2 pf_read_tr16(const uint8_t* p) {
+  const pf_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) pf_h4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // A tile whose fp16 partial row sum (16 scores per lane) stays at or below
 // this keeps the lagging reference max: every p is then <= 2^14, well inside
 // fp16, and O / l need no rescale.
@@ -184,12 +195,13 @@ ATTNQ_DEV void pf_work_item(const PrefillArgs& a, int ntiles, int lin, int& b, i
   }
 }
 
-template <int D, int QM, bool V_F8, bool O_BF16>
+template <int D, int QM, bool V_F8, bool O_BF16, bool PAGED>
 __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const PrefillArgs a) {
   using G = PfGeo<D, V_F8>;
   constexpr bool QK_F8 = QM == PF_Q_FP8 || QM == PF_Q_FP8_MFMA8;  // fp8 codes
   constexpr bool QK_I8 = !QK_F8;                             // int8 QK MFMA
   constexpr bool Q_RAW = QM == PF_Q_RAW_F16 || QM == PF_Q_RAW_BF16;  // Q quantized here
+  static_assert(!PAGED || (QK_F8 && V_F8), "the paged form reads fp8 K and V pages");
   // the DMA ring, then 4 floats for the block-amax exchange of a raw Q
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS + 16];
   const int lane = threadIdx.x & 63;
@@ -201,10 +213,23 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   h = __builtin_amdgcn_readfirstlane(h);
   const int tile = (int)gridDim.x / (a.batch * a.hq) - 1 - ty;
   const int q0 = clampi(a.cu_q[b], 0, a.total_q), q1 = clampi(a.cu_q[b + 1], q0, a.total_q);
-  const int k0 = clampi(a.cu_k[b], 0, a.total_k), k1 = clampi(a.cu_k[b + 1], k0, a.total_k);
+  // keys: a ragged range of K / V^T, or (PAGED) the sequence's page list, its
+  // length (pages - 1) * page_size + the last page's fill (FlashInfer's paged
+  // layout: kv_indptr, kv_indices, kv_last_page_len)
+  int k0 = 0, Lk;
+  int p0 = 0, npg = 0;
+  if constexpr (PAGED) {
+    p0 = __builtin_amdgcn_readfirstlane(a.kv_indptr[b]);
+    npg = __builtin_amdgcn_readfirstlane(max(0, a.kv_indptr[b + 1] - p0));
+    Lk = npg > 0 ? (npg - 1) * a.page_size + clampi(a.kv_last[b], 0, a.page_size) : 0;
+  } else {
+    k0 = clampi(a.cu_k[b], 0, a.total_k);
+    Lk = clampi(a.cu_k[b + 1], k0, a.total_k) - k0;
+  }
   // lengths beyond the host-given maxima would address past the padded V^T
   // rows and the scale arrays: clamp (a broken precondition, not a fault)
-  const int Lq = min(q1 - q0, a.max_q), Lk = min(k1 - k0, a.max_k);
+  const int Lq = min(q1 - q0, a.max_q);
+  Lk = __builtin_amdgcn_readfirstlane(min(Lk, a.max_k));
   constexpr int BM = PfShape<D>::BM;
   const int qs = tile * BM;
   if (qs >= Lq) return;
@@ -281,7 +306,11 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   // the padded V^T block of this (sequence, kv head).
   const long kstride = (long)a.hkv * D;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + ((long)k0 * a.hkv + hk) * D;
-  const __amdgpu_buffer_rsrc_t krs = pf_rsrc(kbase, Lk > 0 ? (uint32_t)((Lk - 1) * kstride + D) : 0u);
+  // PAGED: the whole cache from this kv head's first row on (host-checked
+  // below 2 GiB); each row's page offset goes into its lane's load offset
+  const __amdgpu_buffer_rsrc_t krs =
+      PAGED ? pf_rsrc(kbase, (uint32_t)((long)a.num_pages * a.page_size * kstride - (long)hk * D))
+            : pf_rsrc(kbase, Lk > 0 ? (uint32_t)((Lk - 1) * kstride + D) : 0u);
   const long vrow = (long)a.s_pad * (V_F8 ? 1 : 2);  // bytes per V^T row
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + ((long)b * a.hkv + hk) * D * vrow;
   const __amdgpu_buffer_rsrc_t vrs = pf_rsrc(vbase, (uint32_t)(D * vrow));
@@ -289,12 +318,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   // per-lane byte offsets of the direct loads: wave w fills 1 KB blocks
   // w*N + j of the K (and V^T) stage; lane i of a block writes its chunk i
   uint32_t kvo[G::NKD];
+  int krow[G::NKD];  // PAGED: the tile row of each load (kvo then holds its chunk offset)
 #pragma unroll
   for (int j = 0; j < G::NKD; ++j) {
     const int blk = wave * G::NKD + j;
     const int r = blk * (1024 / D) + lane / G::K_CH;
     const int c = (lane % G::K_CH) ^ G::ksw(r);
-    kvo[j] = (uint32_t)(r * kstride + c * 16);
+    krow[j] = r;
+    kvo[j] = PAGED ? (uint32_t)(c * 16) : (uint32_t)(r * kstride + c * 16);
   }
   uint32_t vvo[G::NVD > 0 ? G::NVD : 1];
 #pragma unroll
@@ -304,26 +335,79 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     const int c = (lane % 8) ^ G::vsw(r);
     vvo[j] = (uint32_t)(r * vrow + c * 16);
   }
-  // fp8 V^T: 16 codes per load, widened to fp16 on the way into LDS
+  // PAGED: cache rows by page.  The (at most 4: page sizes are multiples of
+  // 16) pages that hold keys [64t, 64t + 64) are read through the scalar
+  // cache, with indices clamped into the sequence's page list and page ids
+  // into [0, num_pages).  A row then sits at byte (page * page_size + slot) *
+  // kstride of the cache (plus the kv head's offset).
+  const __attribute__((address_space(4))) int32_t* kv_ix =
+      (const __attribute__((address_space(4))) int32_t*)(uintptr_t)(a.kv_indices + p0);
+  const int ps = a.page_size;
+  struct TilePages {
+    int id[4];
+    int x0;  // position of key 64t inside the first page
+  };
+  auto tile_pages = [&](int t) {
+    TilePages tp;
+    const int first = (t * PF_BN) / ps;
+    tp.x0 = t * PF_BN - first * ps;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tp.id[i] = clampi(kv_ix[min(first + i, npg - 1)], 0, a.num_pages - 1);
+    return tp;
+  };
+  // byte offset of tile row r (r < 64) in the cache
+  auto row_off = [&](const TilePages& tp, int r) -> uint32_t {
+    const int x = tp.x0 + r;
+    const int pi = (x >= ps) + (x >= 2 * ps) + (x >= 3 * ps);
+    const int page = pi == 0 ? tp.id[0] : pi == 1 ? tp.id[1] : pi == 2 ? tp.id[2] : tp.id[3];
+    return (uint32_t)(page * ps + (x - pi * ps)) * (uint32_t)kstride;
+  };
+  // fp8 V: 16 codes per load, widened to fp16 on the way into LDS.  Ragged:
+  // V^T rows (16 keys of one d).  PAGED: token rows (16 d of one key); rows
+  // past the last key are zeros (a stale slot of the last page may hold NaN
+  // codes, and NaN times p = 0 is still NaN).
   u32x4 vreg[G::VC > 0 ? G::VC : 1];
-  auto vload = [&](int t) {
+  auto vload = [&](int t, const TilePages& tp) {
     static_for<0, G::VC>([&](auto ci) {
       constexpr int c = decltype(ci)::value;
       const int idx = threadIdx.x + c * G::THREADS;
-      vreg[c] = *reinterpret_cast<const u32x4*>(vbase + (long)t * PF_BN + (idx >> 2) * vrow + (idx & 3) * 16);
+      if constexpr (PAGED) {
+        const int r = idx / (D / 16), cc = idx % (D / 16);
+        vreg[c] = u32x4{0, 0, 0, 0};
+        if (t * PF_BN + r < Lk)
+          vreg[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) + (long)hk * D +
+                                                    row_off(tp, r) + cc * 16);
+      } else {
+        vreg[c] = *reinterpret_cast<const u32x4*>(vbase + (long)t * PF_BN + (idx >> 2) * vrow + (idx & 3) * 16);
+      }
     });
   };
   auto vstore = [&](int stage) {
     static_for<0, G::VC>([&](auto ci) {
       constexpr int c = decltype(ci)::value;
       const int idx = threadIdx.x + c * G::THREADS;
-      const int r = idx >> 2, j = idx & 3;
       u32x4 lo, hi;
       pf_widen_fp8(vreg[c], lo, hi);
-      uint8_t* row = smem + G::V_OFF + stage * G::VBYTES + r * 128;
-      *reinterpret_cast<u32x4*>(row + ((2 * j) ^ G::vsw(r)) * 16) = lo;
-      *reinterpret_cast<u32x4*>(row + ((2 * j + 1) ^ G::vsw(r)) * 16) = hi;
+      if constexpr (PAGED) {
+        // token-major fp16 rows of D * 2 bytes, 16-byte chunk j of row r at
+        // chunk position j ^ (r % chunks per row)
+        const int r = idx / (D / 16), cc = idx % (D / 16);
+        uint8_t* row = smem + G::V_OFF + stage * G::VBYTES + r * (2 * D);
+        *reinterpret_cast<u32x4*>(row + ((2 * cc) ^ G::tsw(r)) * 16) = lo;
+        *reinterpret_cast<u32x4*>(row + ((2 * cc + 1) ^ G::tsw(r)) * 16) = hi;
+      } else {
+        const int r = idx >> 2, j = idx & 3;
+        uint8_t* row = smem + G::V_OFF + stage * G::VBYTES + r * 128;
+        *reinterpret_cast<u32x4*>(row + ((2 * j) ^ G::vsw(r)) * 16) = lo;
+        *reinterpret_cast<u32x4*>(row + ((2 * j + 1) ^ G::vsw(r)) * 16) = hi;
+      }
     });
+  };
+  // PAGED: the direct-load offsets of tile t (rows past the last key address
+  // beyond the range: zeros)
+  auto kvo_paged = [&](int t, const TilePages& tp, uint32_t (&vo)[G::NKD]) {
+#pragma unroll
+    for (int j = 0; j < G::NKD; ++j) vo[j] = t * PF_BN + krow[j] < Lk ? row_off(tp, krow[j]) + kvo[j] : 0x80000000u;
   };
 
   const uint32_t ktile_bytes = (uint32_t)(PF_BN * kstride);
@@ -336,6 +420,15 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   const int kr1 = n * 128 + (((2 * g + 1) ^ G::ksw(n)) * 16);  // D == 128 only
   const int vr0 = n * 128 + ((g ^ G::vsw(n)) * 16);
   const int vr1 = n * 128 + (((4 + g) ^ G::vsw(n)) * 16);
+  // PAGED: transposed reads of token-major V (ds_read_b64_tr_b16).  In each
+  // 16-lane group g, lane 4k + q names row 4g + k (+ 16h + 32ks) and the 4
+  // values of d = 16db + 4q..; lane n receives d = 16db + n of those 4 rows:
+  // keys 32ks + 16h + 4g + 0..3, the keys of P slots 4h..4h+3 of the lane.
+  const int vtr_row = 4 * g + (n >> 2), vtr_q = n & 3;
+  int vtr[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    vtr[db] = vtr_row * (2 * D) + (((2 * db + (vtr_q >> 1)) ^ G::tsw(vtr_row)) * 16) + (vtr_q & 1) * 8;
 
   // ---- accumulators
   v4f oacc[D / 16][2];
@@ -351,14 +444,26 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
 
   // ---- prologue: tiles 0 and 1 in flight
   constexpr int NPEND = G::NKD + G::NVD;  // direct loads per wave per tile
+  TilePages tp_v{};  // PAGED: the pages of the next V tile to load
   if constexpr (Q_RAW && !V_F8) {
     // unconditional, so that one wait below counts them: loads past the last
     // key read zeros (range-checked descriptors) into stages no tile uses
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
+  } else if (PAGED && n_kt > 0) {
+    const TilePages tp0 = tile_pages(0);
+    uint32_t vo[G::NKD];
+    kvo_paged(0, tp0, vo);
+    pf_dma<D, V_F8>(krs, vrs, vo, vvo, 0u, 0u, kdst(0), vdst(0));
+    vload(0, tp0);
+    if (n_kt > 1) {
+      tp_v = tile_pages(1);
+      kvo_paged(1, tp_v, vo);
+      pf_dma<D, V_F8>(krs, vrs, vo, vvo, 0u, 0u, kdst(1), vdst(1));
+    }
   } else if (n_kt > 0) {
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
-    if constexpr (V_F8) vload(0);
+    if constexpr (V_F8) vload(0, TilePages{});
     if (n_kt > 1) pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
   }
   if constexpr (Q_RAW) {
@@ -417,17 +522,31 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   int kst = 0;  // K (and DMA'd V^T) stage of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
     if constexpr (V_F8) vstore(kt & 1);
+    // PAGED: the pages of tile kt+2, read through the scalar cache before the
+    // barrier's wait covers them
+    TilePages tp_k{};
+    if constexpr (PAGED) {
+      if (kt + 2 < n_kt) tp_k = tile_pages(kt + 2);
+    }
     // tile kt landed (only tile kt+1's direct loads may still be in flight)
     if (kt + 1 < n_kt) pf_wait_vm<NPEND>();
     else pf_wait_vm<0>();
     pf_barrier();
     // the stage of tile kt+2 was last read in tile kt-1: every wave is past it
     if constexpr (V_F8) {
-      if (kt + 1 < n_kt) vload(kt + 1);
+      if (kt + 1 < n_kt) vload(kt + 1, tp_v);
     }
     if (kt + 2 < n_kt) {
       const int st2 = kst == 0 ? 2 : kst - 1;
-      pf_dma<D, V_F8>(krs, vrs, kvo, vvo, (uint32_t)(kt + 2) * ktile_bytes, (uint32_t)(kt + 2) * (PF_BN * 2), kdst(st2), vdst(st2));
+      if constexpr (PAGED) {
+        uint32_t vo[G::NKD];
+        kvo_paged(kt + 2, tp_k, vo);
+        pf_dma<D, V_F8>(krs, vrs, vo, vvo, 0u, 0u, kdst(st2), vdst(st2));
+        tp_v = tp_k;
+      } else {
+        pf_dma<D, V_F8>(krs, vrs, kvo, vvo, (uint32_t)(kt + 2) * ktile_bytes, (uint32_t)(kt + 2) * (PF_BN * 2),
+                        kdst(st2), vdst(st2));
+      }
     }
     const int cur = kst;
     kst = kst == PF_NST - 1 ? 0 : kst + 1;
@@ -498,8 +617,17 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     v8h vop[D / 16][2];
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      vop[db][0] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr0);
-      vop[db][1] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr1);
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x2 lo = pf_read_tr16(sv + vtr[db] + (32 * ks) * (2 * D));
+          const u32x2 hi = pf_read_tr16(sv + vtr[db] + (32 * ks + 16) * (2 * D));
+          vop[db][ks] = __builtin_bit_cast(v8h, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+      } else {
+        vop[db][0] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr0);
+        vop[db][1] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr1);
+      }
     }
 
     float fold;
@@ -638,7 +766,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   }
 }
 
-template <int D, int QM, bool F8>
+template <int D, int QM, bool F8, bool PAGED = false>
 static bool launch_t(const PrefillArgs& args, bool o_bf16, int max_seqlen_q, hipStream_t s) {
   const int tiles = (max_seqlen_q + PfShape<D>::BM - 1) / PfShape<D>::BM;
   if ((long)args.batch * args.hq * tiles > 0x7FFFFFFFL) return false;
@@ -648,9 +776,9 @@ static bool launch_t(const PrefillArgs& args, bool o_bf16, int max_seqlen_q, hip
   a.tblk = max(1, PF_TBLK_WGS / (a.hq / a.hkv));
   dim3 grid((unsigned)(a.batch * a.hq * tiles));
   if (o_bf16)
-    hipLaunchKernelGGL((k_prefill<D, QM, F8, true>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<D, QM, F8, true, PAGED>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_prefill<D, QM, F8, false>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<D, QM, F8, false, PAGED>), grid, dim3(PfShape<D>::THREADS), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -676,6 +804,20 @@ bool launch_prefill(const PrefillArgs& a, int head_dim, int q_mode, bool v_fp8, 
   if (max_seqlen_q <= 0 || a.batch <= 0) return true;
   return head_dim == 128 ? launch_q<128>(a, q_mode, v_fp8, o_bf16, max_seqlen_q, s)
                          : launch_q<64>(a, q_mode, v_fp8, o_bf16, max_seqlen_q, s);
+}
+
+template <int D>
+static bool launch_paged_d(const PrefillArgs& a, int q_mode, bool o_bf16, int max_seqlen_q, hipStream_t s) {
+  return q_mode == PF_Q_FP8_MFMA8 ? launch_t<D, PF_Q_FP8_MFMA8, true, true>(a, o_bf16, max_seqlen_q, s)
+                                  : launch_t<D, PF_Q_FP8, true, true>(a, o_bf16, max_seqlen_q, s);
+}
+
+bool launch_prefill_paged(const PrefillArgs& a, int head_dim, int q_mode, bool o_bf16, int max_seqlen_q,
+                          hipStream_t s) {
+  if (max_seqlen_q <= 0 || a.batch <= 0) return true;
+  if (q_mode != PF_Q_FP8 && q_mode != PF_Q_FP8_MFMA8) return false;
+  return head_dim == 128 ? launch_paged_d<128>(a, q_mode, o_bf16, max_seqlen_q, s)
+                         : launch_paged_d<64>(a, q_mode, o_bf16, max_seqlen_q, s);
 }
 
 }  // namespace attnq

@@ -251,6 +251,49 @@ class PagedPrefill:
         return self.o
 
 
+class PagedPrefillFp8:
+    """A prefill chunk against a paged fp8 e4m3fn cache (the pages and
+    per-head descales attn_decode_paged reads), the pages read inside the
+    attention kernel (FlashInfer's paged prefill run; aiter's
+    flash_attn_with_kvcache with an fp8 cache and a page table): Q gets fp8
+    per-head quantization (attn_quant_qk), then attn_prefill_paged, the
+    chunk's queries aligned to the end of their sequence's cached keys."""
+
+    def __init__(self, q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len, cu_q,
+                 max_q, max_kv_len, sm_scale, causal=True, out_dtype=torch.bfloat16, want_lse=False,
+                 fp8_mma8=False):
+        dev = q.device
+        if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+            raise TypeError("PagedPrefillFp8 takes fp8 e4m3fn caches as uint8 codes")
+        self.q, self.kc, self.vc, self.ks, self.vs = q, k_cache, v_cache, k_scale, v_scale
+        self.ip, self.ix, self.lpl, self.cu_q = kv_indptr, kv_indices, kv_last_page_len, cu_q
+        self.tq, self.hq, self.d = q.shape
+        self.num_pages, self.page_size, self.hkv, _ = k_cache.shape
+        self.b = cu_q.numel() - 1
+        self.max_q, self.max_kv = int(max_q), int(max_kv_len)
+        self.sm_scale, self.causal = _scale(sm_scale), bool(causal)
+        self.mode = A.Q_FP8_PER_HEAD_MFMA8 if fp8_mma8 else A.Q_FP8_PER_HEAD
+        self.qc = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        self.qs = torch.empty(self.hq, dtype=torch.float32, device=dev)
+        self.o = torch.empty((self.tq, self.hq, self.d), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((self.hq, self.tq), dtype=torch.float32, device=dev) if want_lse else None
+
+    def quantize(self):
+        A.attn_quant_qk(self.q, _dtype_code(self.q), self.cu_q, self.b, self.max_q, self.tq, self.hq, self.d,
+                        A.Q_FP8_PER_HEAD, 128, None, self.qc, self.qs)
+
+    def attend(self):
+        A.attn_prefill_paged(self.qc, self.qs, self.mode, self.kc, self.vc, self.ks, self.vs, self.ip, self.ix,
+                             self.lpl, self.cu_q, self.b, self.num_pages, self.page_size, self.max_q, self.max_kv,
+                             self.tq, self.hq, self.hkv, self.d, self.sm_scale, self.causal, self.o,
+                             _dtype_code(self.o), self.lse)
+
+    def run(self):
+        self.quantize()
+        self.attend()
+        return self.o
+
+
 class PagedDecode:
     """Split-KV paged fp8 decode + log-sum-exp merge."""
 

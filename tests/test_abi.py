@@ -145,6 +145,30 @@ def test_decode_validation():
     assert _decode(ws=FAKE + 8) == -1
 
 
+def _ppaged(**kw):
+    a = dict(q=FAKE, qs=FAKE, mode=pk.Q_FP8_PER_HEAD, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, ip=FAKE, ix=FAKE,
+             lpl=FAKE, cu=FAKE, b=2, np_=64, ps=16, mq=100, mk=1000, tq=150, hq=32, hkv=8, d=128, sc=0.1,
+             causal=1, o=FAKE, od=pk.BF16, lse=None, st=None)
+    a.update(kw)
+    return pk.lib().attn_prefill_paged(*a.values())
+
+
+def test_prefill_paged_validation():
+    assert _ppaged(ps=8) == -1 and "page_size" in _err()
+    assert _ppaged(ps=40) == -1
+    assert _ppaged(d=96) == -2 and "head_dim" in _err()
+    assert _ppaged(hq=30, hkv=8) == -1
+    assert _ppaged(mode=pk.Q_INT8_PER_BLOCK) == -2 and "scale_mode" in _err()
+    assert _ppaged(od=pk.FP8E4M3) == -2
+    assert _ppaged(np_=0) == -1 and "num_pages" in _err()
+    assert _ppaged(np_=1 << 14, ps=1024) == -2 and "2 GiB" in _err()
+    assert _ppaged(sc=float("inf")) == -1 and "sm_scale" in _err()
+    assert _ppaged(sc=float("nan"), b=0) == 0      # default scale; nothing to do
+    assert _ppaged(tq=0) == 0
+    assert _ppaged(kc=FAKE + 8) == -1 and "aligned" in _err()
+    assert _ppaged(ix=None) == -1
+
+
 def _gather(**kw):
     a = dict(c=FAKE, eb=2, ip=FAKE, ix=FAKE, lpl=FAKE, cu=FAKE, b=2, mk=100, np_=64, ps=16, hkv=8,
              d=128, out=FAKE, st=None)

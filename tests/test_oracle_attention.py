@@ -424,3 +424,49 @@ def test_mla_fp8_row_decode():
     for c in range(512):
         assert kn[c] == brute.e4m3fn_value(int(row[c])) * float(sc[c // 128])
     assert np.abs(kn).max() <= 3.75 * float(sc.max())
+
+
+# ---------------------------------------------------------------------------
+# paged prefill (fp8 pages)
+# ---------------------------------------------------------------------------
+def _paged_fp8(seed, kv, ql, ps=4, hq=4, hkv=2, d=8):
+    return gen.paged_prefill_fp8_inputs(seed, list(kv), list(ql), hq, hkv, d, page_size=ps, spare_frac=0.5)
+
+
+def _ppf(x, scale, causal, **kw):
+    from oracle.attention import prefill_paged
+    return prefill_paged(x["q"], x["q_scale"], x["k_cache"], x["v_cache"], x["k_scale"], x["v_scale"],
+                         x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], x["cu_q"], scale, causal, **kw)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("kv,ql", [((9, 0, 6, 4), (3, 0, 6, 1)), ((5, 8), (0, 2)), ((3,), (3,))])
+def test_prefill_paged_vs_page_walk(causal, kv, ql):
+    """The composition (pages -> ragged -> dequantize -> prefill_varlen)
+    against a scalar walk over pages and slots with its own fp8 decoder;
+    stale slots and spare pages hold NaN codes."""
+    x = _paged_fp8(11, kv, ql)
+    r = _ppf(x, 0.4, causal)
+    bo, bl = brute.prefill_paged(x["q"], x["q_scale"], x["k_cache"], x["v_cache"], x["k_scale"], x["v_scale"],
+                                 x["kv_indptr"], x["kv_indices"], x["kv_last_page_len"], x["cu_q"], 0.4, causal)
+    assert np.allclose(r["o_exact"], bo, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.isfinite(r["lse"]), np.isfinite(bl))
+    fin = np.isfinite(bl)
+    assert np.allclose(r["lse"][fin], bl[fin], rtol=1e-6)
+    assert not np.isnan(r["o_exact"]).any()
+
+
+def test_prefill_paged_last_query_is_the_decode():
+    """One query per sequence at the last position sees every cached key:
+    with a power-of-two q descale its dequantized value is a bf16 value, and
+    the result is decode_paged's."""
+    x = _paged_fp8(12, (9, 6, 4), (1, 1, 1))
+    x["q_scale"] = np.full(x["q_scale"].shape, 0.5, np.float32)
+    from oracle.numerics import e4m3fn_decode
+    qv = e4m3fn_decode(x["q"]) * 0.5                  # [B, Hq, D], exact in bf16
+    qbits = gen.bf16_bits(qv.astype(np.float32))
+    r = _ppf(x, 0.3, True)
+    dd = decode_paged(qbits, x["k_cache"], x["v_cache"], x["k_scale"], x["v_scale"], x["kv_indptr"],
+                      x["kv_indices"], x["kv_last_page_len"], 0.3)
+    assert np.allclose(r["o_exact"], dd["o_exact"], rtol=1e-13, atol=1e-14)
+    assert np.allclose(r["lse"].T, dd["lse"], rtol=1e-7)
