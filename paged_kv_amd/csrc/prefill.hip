@@ -343,20 +343,32 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   const __attribute__((address_space(4))) int32_t* kv_ix =
       (const __attribute__((address_space(4))) int32_t*)(uintptr_t)(a.kv_indices + p0);
   const int ps = a.page_size;
+  // With page_size a multiple of 64 every tile lies inside one page: its
+  // rows are one wave-uniform page offset plus the row's own offset.
+  const bool one_page = ps % PF_BN == 0;
   struct TilePages {
     int id[4];
-    int x0;  // position of key 64t inside the first page
+    int x0;         // position of key 64t inside the first page
+    uint32_t base;  // one_page: byte offset of key 64t in the cache
   };
   auto tile_pages = [&](int t) {
     TilePages tp;
     const int first = (t * PF_BN) / ps;
     tp.x0 = t * PF_BN - first * ps;
+    if (one_page) {
+      tp.id[0] = clampi(kv_ix[min(first, npg - 1)], 0, a.num_pages - 1);
+      tp.id[1] = tp.id[2] = tp.id[3] = tp.id[0];
+      tp.base = (uint32_t)(tp.id[0] * ps + tp.x0) * (uint32_t)kstride;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tp.id[i] = clampi(kv_ix[min(first + i, npg - 1)], 0, a.num_pages - 1);
+      for (int i = 0; i < 4; ++i) tp.id[i] = clampi(kv_ix[min(first + i, npg - 1)], 0, a.num_pages - 1);
+      tp.base = 0;
+    }
     return tp;
   };
   // byte offset of tile row r (r < 64) in the cache
   auto row_off = [&](const TilePages& tp, int r) -> uint32_t {
+    if (one_page) return tp.base + (uint32_t)r * (uint32_t)kstride;
     const int x = tp.x0 + r;
     const int pi = (x >= ps) + (x >= 2 * ps) + (x >= 3 * ps);
     const int page = pi == 0 ? tp.id[0] : pi == 1 ? tp.id[1] : pi == 2 ? tp.id[2] : tp.id[3];
@@ -403,11 +415,21 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
       }
     });
   };
-  // PAGED: the direct-load offsets of tile t (rows past the last key address
-  // beyond the range: zeros)
-  auto kvo_paged = [&](int t, const TilePages& tp, uint32_t (&vo)[G::NKD]) {
+  // PAGED: the direct-load offsets of tile t, returning the soffset.  One
+  // page per tile: the page offset goes in the soffset, and rows past the
+  // last key read the page's stale slots (their scores are masked by
+  // select, which NaN codes cannot pass).  Else each row's page offset is
+  // in its lane's offset, and rows past the last key address beyond the
+  // range (zeros).
+  auto kvo_paged = [&](int t, const TilePages& tp, uint32_t (&vo)[G::NKD]) -> uint32_t {
+    if (one_page) {
+#pragma unroll
+      for (int j = 0; j < G::NKD; ++j) vo[j] = (uint32_t)krow[j] * (uint32_t)kstride + kvo[j];
+      return tp.base;
+    }
 #pragma unroll
     for (int j = 0; j < G::NKD; ++j) vo[j] = t * PF_BN + krow[j] < Lk ? row_off(tp, krow[j]) + kvo[j] : 0x80000000u;
+    return 0u;
   };
 
   const uint32_t ktile_bytes = (uint32_t)(PF_BN * kstride);
@@ -453,13 +475,13 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   } else if (PAGED && n_kt > 0) {
     const TilePages tp0 = tile_pages(0);
     uint32_t vo[G::NKD];
-    kvo_paged(0, tp0, vo);
-    pf_dma<D, V_F8>(krs, vrs, vo, vvo, 0u, 0u, kdst(0), vdst(0));
+    uint32_t so = kvo_paged(0, tp0, vo);
+    pf_dma<D, V_F8>(krs, vrs, vo, vvo, so, 0u, kdst(0), vdst(0));
     vload(0, tp0);
     if (n_kt > 1) {
       tp_v = tile_pages(1);
-      kvo_paged(1, tp_v, vo);
-      pf_dma<D, V_F8>(krs, vrs, vo, vvo, 0u, 0u, kdst(1), vdst(1));
+      so = kvo_paged(1, tp_v, vo);
+      pf_dma<D, V_F8>(krs, vrs, vo, vvo, so, 0u, kdst(1), vdst(1));
     }
   } else if (n_kt > 0) {
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
@@ -540,8 +562,8 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
       const int st2 = kst == 0 ? 2 : kst - 1;
       if constexpr (PAGED) {
         uint32_t vo[G::NKD];
-        kvo_paged(kt + 2, tp_k, vo);
-        pf_dma<D, V_F8>(krs, vrs, vo, vvo, 0u, 0u, kdst(st2), vdst(st2));
+        const uint32_t so = kvo_paged(kt + 2, tp_k, vo);
+        pf_dma<D, V_F8>(krs, vrs, vo, vvo, so, 0u, kdst(st2), vdst(st2));
         tp_v = tp_k;
       } else {
         pf_dma<D, V_F8>(krs, vrs, kvo, vvo, (uint32_t)(kt + 2) * ktile_bytes, (uint32_t)(kt + 2) * (PF_BN * 2),
