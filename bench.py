@@ -493,11 +493,11 @@ XCD_NUM = 8       # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs
 
 # workload -> summary file, kernel-name patterns of its hot kernels, sources
 COUNTER_WORKLOADS = {
-    "c2": {"file": "counters_k_prefill_sage_varlen.md", "kernels": [r"k_prefill<128, 2, false, false>"],
+    "c2": {"file": "counters_k_prefill_sage_varlen.md", "kernels": [r"k_prefill<128, 2, false, false, false>"],
            "title": "int8-QK / fp16-PV varlen prefill (SageAttention workload: B=8, lengths U{512..4096} seed "
                     "1002, causal, Hq=32, Hkv=8, D=128; 16-bit Q quantized in the kernel)",
            "sources": ("paged_kv_amd/csrc/prefill.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")},
-    "c5": {"file": "counters_k_prefill_fp8_long.md", "kernels": [r"k_prefill<128, 0, false, true>"],
+    "c5": {"file": "counters_k_prefill_fp8_long.md", "kernels": [r"k_prefill<128, 0, false, true, false>"],
            "title": "fp8 prefill, QK^T summed exactly on f16 MFMAs (long workload: B=1, S=32768, H=64, D=128, "
                     "causal, after RoPE + paged append + fp8 quantization)",
            "sources": ("paged_kv_amd/csrc/prefill.hip", "paged_kv_amd/csrc/kcommon.h", "paged_kv_amd/csrc/launch.h")},
