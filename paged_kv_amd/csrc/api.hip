@@ -461,16 +461,12 @@ int scratch_address(void** out) {
   return ATTNQ_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                      const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
-                      const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
-                      int num_pages, int page_size, int num_q_heads, int num_kv_heads,
-                      int head_dim, int max_kv_len, float sm_scale, void* workspace,
-                      size_t workspace_bytes, void* o, float* lse, hipStream_t stream) {
+// The host checks of the paged decode, shared by both of its entry points
+// (everything but the workspace).
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                 const float* v_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
+                 const int32_t* kv_last_page_len, int batch, int num_pages, int page_size, int num_q_heads,
+                 int num_kv_heads, int head_dim, int max_kv_len, float sm_scale, void* o, float* lse) {
   REQUIRE(head_dim == 64 || head_dim == 128, ATTNQ_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0, ATTNQ_EINVAL,
           "num_q_heads must be a positive multiple of num_kv_heads");
@@ -481,7 +477,6 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   REQUIRE(batch <= 65535, ATTNQ_EUNSUPPORTED, "batch must be <= 65535");
   REQUIRE(num_pages > 0, ATTNQ_EINVAL, "num_pages must be positive");
   REQUIRE(scale_ok(sm_scale), ATTNQ_EINVAL, "sm_scale must be finite (or NaN for 1/sqrt(head_dim))");
-  sm_scale = scale_or_default(sm_scale, head_dim);
   if (batch == 0) return ok();
   REQUIRE_PTR(q, 16);
   REQUIRE_PTR(k_cache, 16);
@@ -493,6 +488,23 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   REQUIRE_PTR(kv_last_page_len, 4);
   REQUIRE_PTR(o, 16);
   REQUIRE_OPT_PTR(lse, 4);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, const int32_t* kv_last_page_len, int batch,
+                      int num_pages, int page_size, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_kv_len, float sm_scale, void* workspace,
+                      size_t workspace_bytes, void* o, float* lse, hipStream_t stream) {
+  const int st = decode_check(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len, batch,
+                              num_pages, page_size, num_q_heads, num_kv_heads, head_dim, max_kv_len, sm_scale, o, lse);
+  if (st != ATTNQ_OK || batch == 0) return st;
+  sm_scale = scale_or_default(sm_scale, head_dim);
   REQUIRE_PTR(workspace, 256);
   const size_t need = attn_decode_paged_workspace_size(batch, num_q_heads, head_dim, max_kv_len, page_size);
   REQUIRE(workspace_bytes >= need, ATTNQ_EWORKSPACE, "workspace too small: %zu < %zu bytes",
@@ -522,6 +534,10 @@ int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_
                               int num_pages, int page_size, int num_q_heads, int num_kv_heads,
                               int head_dim, int max_kv_len, float sm_scale, void* o, float* lse,
                               hipStream_t stream) {
+  // arguments first: the scratch array is looked up only for a call that runs
+  const int st = decode_check(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len, batch,
+                              num_pages, page_size, num_q_heads, num_kv_heads, head_dim, max_kv_len, sm_scale, o, lse);
+  if (st != ATTNQ_OK || batch == 0) return st;
   // the partials need no clearing: the merge reads exactly the chunks the
   // split phase of this call writes
   const size_t need = attn_decode_paged_workspace_size(batch, num_q_heads, head_dim, max_kv_len, page_size);
@@ -529,10 +545,8 @@ int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_
           "attn_decode_paged_noalloc: the split partials need %zu bytes, more than the library's fixed "
           "scratch of %zu bytes (use attn_decode_paged with a workspace)", need, kNoAllocScratchBytes);
   void* ws = nullptr;
-  if (batch > 0) {
-    const int st = scratch_address(&ws);
-    if (st != ATTNQ_OK) return st;
-  }
+  const int sst = scratch_address(&ws);
+  if (sst != ATTNQ_OK) return sst;
   return attn_decode_paged(q, k_cache, v_cache, k_scale, v_scale, kv_indptr, kv_indices, kv_last_page_len,
                            batch, num_pages, page_size, num_q_heads, num_kv_heads, head_dim, max_kv_len,
                            sm_scale, ws, kNoAllocScratchBytes, o, lse, stream);

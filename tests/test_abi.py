@@ -131,6 +131,17 @@ def _decode(**kw):
     return pk.lib().attn_decode_paged(*a.values())
 
 
+def test_decode_noalloc_validates_before_touching_a_device():
+    # argument errors come first, whatever the device state (no GPU here)
+    L = pk.lib()
+    assert L.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 16, 32, 8, 96, 100,
+                                       0.1, FAKE, None, None) == -2 and "head_dim" in _err()
+    assert L.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 32, 8, 128, 100,
+                                       0.1, FAKE, None, None) == -1 and "page_size" in _err()
+    assert L.attn_decode_paged_noalloc(None, None, None, None, None, None, None, None, 0, 10, 16, 32, 8, 128, 100,
+                                       0.1, None, None, None) == 0
+
+
 def test_decode_validation():
     assert _decode(ps=8) == -1 and "page_size" in _err()
     assert _decode(ps=2048) == -1
