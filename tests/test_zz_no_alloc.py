@@ -71,7 +71,8 @@ def test_no_alloc_decode_rejects_sizes_past_the_scratch():
     x = gen.paged_decode_inputs(93, [64], 8, 8, 128)
     q, kc, vc, ks, vs, ip, ix, lpl = _inputs(x)
     o = torch.empty((1, 8, 128), dtype=torch.bfloat16, device="cuda")
-    # 512 q heads x (2^20 tokens / 512) chunks x 129 floats: 528 MiB of partials
+    # 128 q heads x (2^20 tokens / 512) chunks x 129 floats: 129 MiB of partials
+    # (valid arguments otherwise: they are checked before the size)
     with pytest.raises(RuntimeError, match="scratch"):
-        A.attn_decode_paged_noalloc(q, kc, vc, ks, vs, ip, ix, lpl, 1, x["num_pages"], 16, 512, 8, 128, 1 << 20,
+        A.attn_decode_paged_noalloc(q, kc, vc, ks, vs, ip, ix, lpl, 1, x["num_pages"], 16, 128, 8, 128, 1 << 20,
                                     0.1, o, None)
