@@ -9,7 +9,8 @@
 // on a 1-D grid whose order (pf_work_item) starts the tiles with the most
 // visible keys first and keeps the q heads of one kv head on one XCD.  Each
 // wave owns 32 queries and streams 64-key tiles staged in LDS by direct
-// loads (three-stage ring).
+// loads (a ring of two stages, or of three K stages when fp8 V is widened
+// through registers).
 //
 // Per key tile and wave:
 //   S^T = K Q^T          fp8 codes widened to fp16 (exact) and f16 16x16x32
@@ -25,6 +26,12 @@
 //                        fp16 P fed to the PV MFMA;
 //   O^T += V^T P^T       fp16 16x16x32 MFMA; P is rounded to fp16, fp8 V codes
 //                        are widened to fp16 (exactly) when staged into LDS.
+//                        With fp16 V^T the operands are read from LDS one
+//                        16-dim block at a time inside the product: holding
+//                        them all across the softmax costs 64 VGPRs, and with
+//                        them the third workgroup per CU.  The fp8-V forms
+//                        run two workgroups per CU either way and read them
+//                        while the softmax runs (8% faster there).
 // Because S^T's accumulator layout (lane n of each 16-lane row holds query n,
 // keys 4g..4g+3) is the B-operand layout of the PV product, P never leaves
 // registers.  V^T arrives permuted (attn_quant_v_permute) so that the 8 keys a
@@ -42,10 +49,16 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// Workgroup shape: each wave owns 32 queries; 4 waves (128 queries), two
-// workgroups per CU.  (8 waves / 256 queries halve the K/V tile traffic but
-// leave one workgroup per CU, whose barriers nothing covers: measured slower
-// on the varlen workload, about even on the long one.)
+// Workgroup shape: each wave owns 32 queries; 4 waves (128 queries).  With
+// fp16 V^T the kernel fits three workgroups per CU (at most 168 VGPRs, 48 KB
+// of LDS in a two-stage ring); the fp8-V forms hold more registers and a
+// third K stage and run two.  More resident waves matter more here than a
+// deeper ring: one workgroup per CU runs the varlen workload 1.7x slower than
+// two, and three are 6% faster than two with three stages.  (8 waves / 256
+// queries halve the K/V tile traffic but leave one workgroup per CU, whose
+// barriers nothing covers: measured slower on the varlen workload, about even
+// on the long one.  8 waves of 16 queries each, two workgroups per CU, read
+// the K and V tiles from LDS twice as often per query: 7-10% slower.)
 template <int D>
 struct PfShape {
   static constexpr int WAVES = 4;
@@ -53,8 +66,8 @@ struct PfShape {
   static constexpr int BM = WAVES * 32;  // queries per workgroup
 };
 constexpr int PF_BN = 64;   // keys per tile
-constexpr int PF_NST = 3;   // LDS stages of the DMA ring (two tiles in flight)
-constexpr int PF_TBLK_WGS = 64;  // workgroups per K/V stream in one block of the work order
+constexpr int PF_NST = 3;   // K stages of the fp8-V ring (two tiles in flight)
+constexpr int PF_XCD_CUS = 32;  // CUs per XCD
 constexpr float PF_LN2 = 0.69314718055994530942f;
 // buffer descriptor word 3 for untyped 32-bit accesses
 constexpr int PF_RSRC_W3 = 0x00020000;
@@ -75,10 +88,12 @@ struct PfGeo {
   static constexpr int NKD = KBYTES / 1024 / WAVES;                // K direct loads per wave per tile
   static constexpr int NVD = V_F8 ? 0 : VBYTES / 1024 / WAVES;     // V^T direct loads per wave per tile
   static_assert(NKD >= 1 && (V_F8 || NVD >= 1), "every wave takes a share of each tile");
-  static constexpr int NV_ST = V_F8 ? 2 : PF_NST;      // V^T stages (fp8 V is widened through registers)
+  static constexpr int NST = V_F8 ? PF_NST : 2;     // K (and DMA'd V^T) stages of the ring
+  static constexpr int DIST = NST - 1;              // tiles in flight ahead of the current one
+  static constexpr int NV_ST = V_F8 ? 2 : NST;      // V^T stages (fp8 V is widened through registers)
   static constexpr int VC = V_F8 ? D * PF_BN / 16 / THREADS : 0;     // fp8 V^T u32x4 per thread
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = PF_NST * KBYTES;
+  static constexpr int V_OFF = NST * KBYTES;
   static constexpr int LDS = V_OFF + NV_ST * VBYTES;
   static ATTNQ_DEV int ksw(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
   static ATTNQ_DEV int vsw(int r) { return (r >> 1) & 7; }
@@ -196,12 +211,14 @@ ATTNQ_DEV void pf_work_item(const PrefillArgs& a, int ntiles, int lin, int& b, i
 }
 
 template <int D, int QM, bool V_F8, bool O_BF16, bool PAGED>
-__global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const PrefillArgs a) {
+__global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(const PrefillArgs a) {
   using G = PfGeo<D, V_F8>;
   constexpr bool QK_F8 = QM == PF_Q_FP8 || QM == PF_Q_FP8_MFMA8;  // fp8 codes
   constexpr bool QK_I8 = !QK_F8;                             // int8 QK MFMA
   constexpr bool Q_RAW = QM == PF_Q_RAW_F16 || QM == PF_Q_RAW_BF16;  // Q quantized here
   static_assert(!PAGED || (QK_F8 && V_F8), "the paged form reads fp8 K and V pages");
+  constexpr bool V_EARLY = V_F8;  // V^T operands read before the softmax
+  static_assert(!PAGED || G::DIST == 2, "the paged form keeps the V pages of tile kt+1 from the K loads of kt+2");
   // the DMA ring, then 4 floats for the block-amax exchange of a raw Q
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS + 16];
   const int lane = threadIdx.x & 63;
@@ -464,14 +481,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   float l_run[2] = {0.f, 0.f};              // lane-local partial row sums
   const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
 
-  // ---- prologue: tiles 0 and 1 in flight
+  // ---- prologue: the first DIST tiles in flight
   constexpr int NPEND = G::NKD + G::NVD;  // direct loads per wave per tile
   TilePages tp_v{};  // PAGED: the pages of the next V tile to load
   if constexpr (Q_RAW && !V_F8) {
     // unconditional, so that one wait below counts them: loads past the last
     // key read zeros (range-checked descriptors) into stages no tile uses
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
-    pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
+    if constexpr (G::DIST == 2) pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
   } else if (PAGED && n_kt > 0) {
     const TilePages tp0 = tile_pages(0);
     uint32_t vo[G::NKD];
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   } else if (n_kt > 0) {
     pf_dma<D, V_F8>(krs, vrs, kvo, vvo, 0u, 0u, kdst(0), vdst(0));
     if constexpr (V_F8) vload(0, TilePages{});
-    if (n_kt > 1) pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
+    if (G::DIST == 2 && n_kt > 1) pf_dma<D, V_F8>(krs, vrs, kvo, vvo, ktile_bytes, PF_BN * 2, kdst(1), vdst(1));
   }
   if constexpr (Q_RAW) {
     // This workgroup's 128 queries are one quantization block (128 tokens
@@ -495,7 +512,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     // writes in INT8_PER_BLOCK mode (same arithmetic, same helpers).  The Q
     // loads went out before the first tiles' loads: wait for them only.
     if constexpr (V_F8) pf_wait_vm<0>();
-    else pf_wait_vm<2 * NPEND>();
+    else pf_wait_vm<G::DIST * NPEND>();
     constexpr bool BF = QM == PF_Q_RAW_BF16;
     float m = 0.0f;
 #pragma unroll
@@ -544,34 +561,35 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
   int kst = 0;  // K (and DMA'd V^T) stage of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
     if constexpr (V_F8) vstore(kt & 1);
-    // PAGED: the pages of tile kt+2, read through the scalar cache before the
-    // barrier's wait covers them
+    // PAGED: the pages of tile kt+DIST, read through the scalar cache before
+    // the barrier's wait covers them
     TilePages tp_k{};
     if constexpr (PAGED) {
-      if (kt + 2 < n_kt) tp_k = tile_pages(kt + 2);
+      if (kt + G::DIST < n_kt) tp_k = tile_pages(kt + G::DIST);
     }
-    // tile kt landed (only tile kt+1's direct loads may still be in flight)
-    if (kt + 1 < n_kt) pf_wait_vm<NPEND>();
+    // tile kt landed (with three stages, tile kt+1's direct loads may still be
+    // in flight)
+    if (G::DIST == 2 && kt + 1 < n_kt) pf_wait_vm<NPEND>();
     else pf_wait_vm<0>();
     pf_barrier();
-    // the stage of tile kt+2 was last read in tile kt-1: every wave is past it
+    // the stage of tile kt+DIST was last read in tile kt-1: every wave is past it
     if constexpr (V_F8) {
       if (kt + 1 < n_kt) vload(kt + 1, tp_v);
     }
-    if (kt + 2 < n_kt) {
-      const int st2 = kst == 0 ? 2 : kst - 1;
+    if (kt + G::DIST < n_kt) {
+      const int st2 = G::NST == 2 ? 1 - kst : (kst == 0 ? 2 : kst - 1);
       if constexpr (PAGED) {
         uint32_t vo[G::NKD];
-        const uint32_t so = kvo_paged(kt + 2, tp_k, vo);
+        const uint32_t so = kvo_paged(kt + G::DIST, tp_k, vo);
         pf_dma<D, V_F8>(krs, vrs, vo, vvo, so, 0u, kdst(st2), vdst(st2));
         tp_v = tp_k;
       } else {
-        pf_dma<D, V_F8>(krs, vrs, kvo, vvo, (uint32_t)(kt + 2) * ktile_bytes, (uint32_t)(kt + 2) * (PF_BN * 2),
+        pf_dma<D, V_F8>(krs, vrs, kvo, vvo, (uint32_t)(kt + G::DIST) * ktile_bytes, (uint32_t)(kt + G::DIST) * (PF_BN * 2),
                         kdst(st2), vdst(st2));
       }
     }
     const int cur = kst;
-    kst = kst == PF_NST - 1 ? 0 : kst + 1;
+    kst = kst == G::NST - 1 ? 0 : kst + 1;
     const int kfirst = kt * PF_BN;
     if (kfirst >= wave_kend) continue;  // every key of this tile is masked for this wave
     const uint8_t* sk = smem + G::K_OFF + cur * G::KBYTES;
@@ -635,21 +653,24 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    // V^T operands of this tile, read while the softmax runs
-    v8h vop[D / 16][2];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
+    // V^T operands of a 16-dim block
+    auto vread = [&](int db, v8h* dst) {
       if constexpr (PAGED) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const u32x2 lo = pf_read_tr16(sv + vtr[db] + (32 * ks) * (2 * D));
           const u32x2 hi = pf_read_tr16(sv + vtr[db] + (32 * ks + 16) * (2 * D));
-          vop[db][ks] = __builtin_bit_cast(v8h, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          dst[ks] = __builtin_bit_cast(v8h, u32x4{lo[0], lo[1], hi[0], hi[1]});
         }
       } else {
-        vop[db][0] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr0);
-        vop[db][1] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr1);
+        dst[0] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr0);
+        dst[1] = *reinterpret_cast<const v8h*>(sv + db * 2048 + vr1);
       }
+    };
+    v8h vop[V_EARLY ? D / 16 : 1][2];
+    if constexpr (V_EARLY) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) vread(db, vop[db]);
     }
 
     float fold;
@@ -740,17 +761,20 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, 2) void k_prefill(const Prefil
     // ---- O^T += V^T P^T
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
+    for (int db = 0; db < D / 16; ++db) {
+      v8h vl[2];
+      if constexpr (!V_EARLY) vread(db, vl);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db][ks], pk[qb][ks], oacc[db][qb], 0, 0, 0);
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(V_EARLY ? vop[db][ks] : vl[ks], pk[qb][ks], oacc[db][qb], 0, 0, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
   }
   // No direct load may outlive the workgroup's LDS.  The last tile waits for
   // every load it issued; this covers a workgroup whose loop never ran (no
-  // visible key: n_kt == 0) after the raw-Q prologue issued two tiles anyway.
+  // visible key: n_kt == 0) after the raw-Q prologue issued its tiles anyway.
   pf_wait_vm<0>();
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
@@ -793,9 +817,17 @@ static bool launch_t(const PrefillArgs& args, bool o_bf16, int max_seqlen_q, hip
   const int tiles = (max_seqlen_q + PfShape<D>::BM - 1) / PfShape<D>::BM;
   if ((long)args.batch * args.hq * tiles > 0x7FFFFFFFL) return false;
   PrefillArgs a = args;
-  // blocks of PF_TBLK_WGS / group tiles: about that many workgroups of one
-  // (sequence, kv head) stream run side by side on an XCD
-  a.tblk = max(1, PF_TBLK_WGS / (a.hq / a.hkv));
+  // blocks of (workgroups resident on an XCD) / group tiles: about that many
+  // workgroups of one (sequence, kv head) stream run side by side on an XCD
+  // (three per CU with fp16 V^T, two with fp8 V at head_dim 128)
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_prefill<D, QM, F8, true, PAGED>, PfShape<D>::THREADS,
+                                                     0) != hipSuccess || n < 1)
+      n = 2;
+    return n;
+  }();
+  a.tblk = max(1, PF_XCD_CUS * per_cu / (a.hq / a.hkv));
   dim3 grid((unsigned)(a.batch * a.hq * tiles));
   if (o_bf16)
     hipLaunchKernelGGL((k_prefill<D, QM, F8, true, PAGED>), grid, dim3(PfShape<D>::THREADS), 0, s, a);

@@ -33,8 +33,11 @@ def work_item(batch, hq, hkv, tblk, ntiles, lin):
 @pytest.mark.parametrize("batch,hq,hkv", [(1, 8, 8), (3, 32, 8), (8, 32, 8), (2, 64, 16), (5, 16, 16),
                                           (4, 12, 4), (1, 2, 2), (7, 6, 3)])
 @pytest.mark.parametrize("ntiles", [1, 2, 3, 7, 33])
-def test_prefill_work_order_is_a_bijection(batch, hq, hkv, ntiles):
-    tblk = max(1, 64 // (hq // hkv))     # the launcher's choice
+@pytest.mark.parametrize("per_cu", [1, 2, 3, 4])
+def test_prefill_work_order_is_a_bijection(batch, hq, hkv, ntiles, per_cu):
+    # the launcher's choice: the workgroups resident on one XCD (32 CUs times
+    # the kernel's occupancy) divided by the group size
+    tblk = max(1, 32 * per_cu // (hq // hkv))
     n = batch * hq * ntiles
     seen = set()
     for lin in range(n):
@@ -49,7 +52,7 @@ def test_longest_tiles_start_first_on_each_xcd():
     # index counted from the sequence end, divided by the block size) never
     # decreases, so the tiles with the most keys are dealt first
     batch, hq, hkv, ntiles = 3, 32, 8, 9
-    tblk = 64 // (hq // hkv)
+    tblk = 96 // (hq // hkv)
     for xcd in range(8):
         blocks = [work_item(batch, hq, hkv, tblk, ntiles, lin)[2] // tblk
                   for lin in range(xcd, batch * hq * ntiles, 8)]
