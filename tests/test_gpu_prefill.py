@@ -136,6 +136,41 @@ def test_sage_int8_small(lens, fuse_q):
     compare_lse(p.lse.cpu().numpy(), ref["lse"], "sage")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("fuse_q", [True, False])
+def test_sage_int8_block_scales_far_apart(causal, fuse_q):
+    """K blocks of one sequence at magnitudes 2^-6 .. 2^6 in a shuffled order
+    (the fold of a later tile can be far above or below the current
+    reference's), one sequence at about 300x (a fold above 1: the kernel then
+    takes the tile without its exact-reference bias) and one at 1e-3x: every
+    case against the oracle."""
+    lens = [1300, 700, 300, 129]
+    x = gen.sage_inputs(47, lens, 8, 2, 128)
+    cu = x["cu_seqlens"]
+    rng = np.random.default_rng(5)
+    k = as_f32(x["k"], "fp16")
+    q = as_f32(x["q"], "fp16")
+    s0 = int(cu[0])
+    nb = (lens[0] + 127) // 128
+    f = 2.0 ** rng.permutation(np.linspace(-6, 6, nb))
+    for j in range(nb):
+        k[s0 + 128 * j:min(s0 + 128 * (j + 1), int(cu[1]))] *= f[j]
+    q[cu[1]:cu[2]] *= 300.0
+    k[cu[1]:cu[2]] *= 300.0
+    q[cu[2]:cu[3]] *= 1e-3
+    x["q"], x["k"] = q.astype(np.float16), k.astype(np.float16)
+    assert np.isfinite(x["q"]).all() and np.isfinite(x["k"]).all()
+    sm = 1 / math.sqrt(128)
+    p, mx = _sage_flow(x, sm, causal=causal, fuse_q=fuse_q)
+    qc, qs, kc, ks = _sage_ref(x, mx, sm, causal)
+    ref = prefill_varlen(dequant_int8_per_block(qc, qs, cu), dequant_int8_per_block(kc, ks, cu),
+                         as_f32(x["v"], "fp16").astype(np.float64), cu, cu, sm, causal, "fp16")
+    got = decode_out(from_dev_bits(p.o), "fp16")
+    stats = compare_outputs(got, ref["o"], ref["o_exact"], "fp16", f"sage scales causal={causal}")
+    compare_lse(p.lse.cpu().numpy(), ref["lse"], "sage scales")
+    print("sage block scales", causal, fuse_q, stats)
+
+
 @pytest.mark.parametrize("case", ["config2", "d64_bf16", "ragged_gqa"])
 def test_sage_fused_q_equals_separate_quant(case):
     """Quantizing Q inside the prefill gives bit-identical outputs, lse and
