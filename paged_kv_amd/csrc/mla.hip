@@ -66,6 +66,7 @@ struct MlaLds {
   MlaStage buf[MLA_NBUF];
   v4f xs[4][2][4][64];            // partial scores [head block][16-token block][channel tile][lane]
   int row_idx[MLA_SPLIT_TOKENS];  // cache row of each selected index, -1 if unused
+  float mask[MLA_SPLIT_TOKENS];   // 0 for a used slot, -inf otherwise (added to its logits)
 };
 
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
         }
       }
       L.row_idx[e] = r;
+      L.mask[e] = r >= 0 ? 0.0f : -INFINITY;
     }
   }
 
@@ -257,15 +259,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       __syncthreads();
       continue;
     }
-    // used indices of the step: bit e of `mine` is token 4g + e of the step
-    const uint64_t used = __ballot(lane < MLA_STEP && L.row_idx[st * MLA_STEP + (lane & (MLA_STEP - 1))] >= 0);
-    const uint32_t mine = (uint32_t)(used >> (4 * g));
+    // logits of the lane's tokens 16j + 4g + r: the mask adds -inf to an
+    // unused slot, whose staged row (codes, scales, rope) is all zeros, so
+    // its score is 0 and the sum -inf for any sm_scale
     float s[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const v4f tot = (xs[hb][j][0][lane] + xs[hb][j][1][lane]) + (xs[hb][j][2][lane] + xs[hb][j][3][lane]);
+      const float* mk = &L.mask[st * MLA_STEP + 16 * j + 4 * g];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[j][r] = (mine >> (16 * j + r)) & 1u ? tot[r] * a.sm_scale_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) s[j][r] = __builtin_fmaf(tot[r], a.sm_scale_log2, mk[r]);
     }
 
     // ---- softmax against a lagging reference max (the four waves of a
