@@ -490,6 +490,7 @@ COUNTER_PASSES = {
 }
 SIMD_NUM = 1024   # 256 CUs x 4 SIMDs
 XCD_NUM = 8       # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs
+PUBLISHED_GHZ = 2.4  # engine clock of the published peaks
 
 # workload -> summary file, kernel-name patterns of its hot kernels, sources
 COUNTER_WORKLOADS = {
@@ -668,10 +669,22 @@ def summarize_counters(wl, run_dir):
     if "mfma" in durs:
         grbm = vals["GRBM_GUI_ACTIVE[mfma]"] / XCD_NUM          # cycles of one XCD
         util = 100.0 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm * SIMD_NUM)
+        # the same busy cycles over the dispatch time at the published clock
+        # (a lower bound: the clock under load is at most that)
+        util_t = 100.0 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMD_NUM * durs["mfma"] * PUBLISHED_GHZ)
+        clock = grbm / max(durs["mfma"], 1.0)
         coexec = 100.0 * vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(vals["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0)
-        derived["mfma_util_pct"] = util
+        # GRBM_GUI_ACTIVE runs ahead of the dispatch for short launches under
+        # counter collection (an implied clock above the published one): then
+        # the dispatch-time figure is the one to use
+        derived["mfma_util_pct"] = util if clock <= PUBLISHED_GHZ else util_t
         lines += [f"- MFMA pipe busy (rocprof's MfmaUtil: sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE of one XCD "
-                  f"x {SIMD_NUM} SIMDs)): **{util:.1f}%**",
+                  f"x {SIMD_NUM} SIMDs)): **{util:.1f}%**"
+                  + ("" if clock <= PUBLISHED_GHZ else
+                     f" -- not usable here: the implied clock ({clock:.2f} GHz) is above the published "
+                     f"{PUBLISHED_GHZ} GHz, i.e. GRBM_GUI_ACTIVE counted well beyond the dispatch"),
+                  f"- MFMA pipe busy over the summed dispatch time ({durs['mfma'] / 1e3:.1f} us) at {PUBLISHED_GHZ} GHz: "
+                  f"**{util_t:.1f}%** (a lower bound)",
                   f"- cycles with a VALU instruction issued beside a busy MFMA pipe: {coexec:.1f}% of the MFMA busy cycles",
                   f"- VALU instructions per MFMA instruction: {vals['SQ_INSTS_VALU'] / max(vals['SQ_INSTS_MFMA'], 1):.2f} "
                   f"(transcendental fp32: {vals['SQ_INSTS_VALU_TRANS_F32'] / max(vals['SQ_INSTS_MFMA'], 1):.2f})",
