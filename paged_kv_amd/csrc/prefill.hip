@@ -17,8 +17,10 @@
 //                        MFMAs (an fp32-exact sum; the fp8 16x16x128 MFMA sums
 //                        its 128 products to only ~2^-12 of sum |q_d k_d|,
 //                        available as a separate Q/K form), or two int8
-//                        16x16x64 (exact i32); the codes' scales and
-//                        sm_scale*log2(e) are folded into one multiplier per tile;
+//                        16x16x64 (exact, accumulated onto the bits of a float
+//                        bias so no conversion is needed); the codes' scales
+//                        and sm_scale*log2(e) are folded into one multiplier
+//                        per tile;
 //   online softmax       one fma + exp2 per score against a lagging reference
 //                        max, moved (tile max across the 4 lanes that hold one
 //                        query; O and l rescale) only when a tile's partial
