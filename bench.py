@@ -515,11 +515,19 @@ COUNTER_WORKLOADS = {
 
 
 def kernel_source_hash(sources) -> str:
+    """Hash of the kernel sources with comments and blank lines removed (a
+    comment edit does not change what the counters measured; the sources
+    hold no string literal with a comment marker in it)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sources:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line.strip():
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
