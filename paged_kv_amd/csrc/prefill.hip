@@ -693,18 +693,14 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
     // fma(PF_BIAS + s, fold, -(bfold + m_ref)) is s * fold - m_ref rounded
     // once: the exp2 argument of an unbiased score.
     float bfold = 0.0f;
-    bool bump = false;  // the fold needs a coarser reference grid
+    int grid_t = -125;
     bool big = false;   // a grid above 1 would shift p too far: no bias
     if constexpr (QK_I8) {
       const uint32_t fb = (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, fold)) + 2u) & ~3u;
       fold = __builtin_bit_cast(float, fb);
       bfold = PF_BIAS * fold;
-      const int grid_t = max((int)((fb >> 23) & 0xffu) - 126, -125);
+      grid_t = max((int)((fb >> 23) & 0xffu) - 126, -125);
       big = grid_t > 0;
-      if (!big && grid_t > m_grid) {
-        m_grid = grid_t;
-        bump = true;
-      }
     }
 
     // ---- mask (tiles that cross the causal diagonal or the sequence end,
@@ -726,7 +722,13 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
           }
       fold = 1.0f;
       bfold = 0.0f;
-      bump = false;
+    }
+    // a biased tile whose fold needs a coarser reference grid than the rows'
+    // references are on goes through the exact path, which moves them up to it
+    bool bump = false;
+    if (QK_I8 && !need_mask && !big && grid_t > m_grid) {
+      m_grid = grid_t;
+      bump = true;
     }
 
     // ---- online softmax against a lagging reference max.  Common path:
