@@ -136,16 +136,17 @@ def test_sage_int8_small(lens, fuse_q):
     compare_lse(p.lse.cpu().numpy(), ref["lse"], "sage")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("fuse_q", [True, False])
-def test_sage_int8_block_scales_far_apart(causal, fuse_q):
+def test_sage_int8_block_scales_far_apart(causal, fuse_q, d):
     """K blocks of one sequence at magnitudes 2^-6 .. 2^6 in a shuffled order
     (the fold of a later tile can be far above or below the current
     reference's), one sequence at about 300x (a fold above 1: the kernel then
     takes the tile without its exact-reference bias) and one at 1e-3x: every
     case against the oracle."""
     lens = [1300, 700, 300, 129]
-    x = gen.sage_inputs(47, lens, 8, 2, 128)
+    x = gen.sage_inputs(47, lens, 8, 2, d)
     cu = x["cu_seqlens"]
     rng = np.random.default_rng(5)
     k = as_f32(x["k"], "fp16")
@@ -160,15 +161,15 @@ def test_sage_int8_block_scales_far_apart(causal, fuse_q):
     q[cu[2]:cu[3]] *= 1e-3
     x["q"], x["k"] = q.astype(np.float16), k.astype(np.float16)
     assert np.isfinite(x["q"]).all() and np.isfinite(x["k"]).all()
-    sm = 1 / math.sqrt(128)
+    sm = 1 / math.sqrt(d)
     p, mx = _sage_flow(x, sm, causal=causal, fuse_q=fuse_q)
     qc, qs, kc, ks = _sage_ref(x, mx, sm, causal)
     ref = prefill_varlen(dequant_int8_per_block(qc, qs, cu), dequant_int8_per_block(kc, ks, cu),
                          as_f32(x["v"], "fp16").astype(np.float64), cu, cu, sm, causal, "fp16")
     got = decode_out(from_dev_bits(p.o), "fp16")
-    stats = compare_outputs(got, ref["o"], ref["o_exact"], "fp16", f"sage scales causal={causal}")
+    stats = compare_outputs(got, ref["o"], ref["o_exact"], "fp16", f"sage scales d={d} causal={causal}")
     compare_lse(p.lse.cpu().numpy(), ref["lse"], "sage scales")
-    print("sage block scales", causal, fuse_q, stats)
+    print("sage block scales", d, causal, fuse_q, stats)
 
 
 @pytest.mark.parametrize("case", ["config2", "d64_bf16", "ragged_gqa"])
