@@ -17,8 +17,10 @@
 //                        MFMAs (an fp32-exact sum; the fp8 16x16x128 MFMA sums
 //                        its 128 products to only ~2^-12 of sum |q_d k_d|,
 //                        available as a separate Q/K form), or two int8
-//                        16x16x64 (exact i32); the codes' scales and
-//                        sm_scale*log2(e) are folded into one multiplier per tile;
+//                        16x16x64 (exact, accumulated onto the bits of a float
+//                        bias so no conversion is needed); the codes' scales
+//                        and sm_scale*log2(e) are folded into one multiplier
+//                        per tile;
 //   online softmax       one fma + exp2 per score against a lagging reference
 //                        max, moved (tile max across the 4 lanes that hold one
 //                        query; O and l rescale) only when a tile's partial
@@ -174,6 +176,10 @@ ATTNQ_DEV u32x2 pf_read_tr16(const uint8_t* p) {
 // this keeps the lagging reference max: every p is then <= 2^14, well inside
 // fp16, and O / l need no rescale.
 constexpr float PF_TILE_SUM_MAX = 16384.0f;
+
+// int8 scores are accumulated onto the bits of this float (1.5 * 2^23)
+constexpr float PF_BIAS = 12582912.0f;
+constexpr int PF_BIAS_BITS = 0x4B400000;
 
 // Work item (sequence b, q head h, query tile counted from the sequence end
 // ty) of linear workgroup id lin; ntiles query tiles per (sequence, head).
@@ -559,6 +565,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
   }
 
   int kst = 0;  // K (and DMA'd V^T) stage of tile kt
+  int m_grid = -126;  // int8: every finite m_ref is a multiple of 2^m_grid (wave-uniform)
   for (int kt = 0; kt < n_kt; ++kt) {
     if constexpr (V_F8) vstore(kt & 1);
     // PAGED: the pages of tile kt+DIST, read through the scalar cache before
@@ -616,21 +623,21 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if constexpr (QK_I8) {
-          // The integer sum (|s| < 2^21) converts to float exactly.  (A
-          // float bias in the accumulator would save this conversion, but the
-          // bias times the tile's scale is then rounded inside the exp2
-          // argument: an error of up to ~1.5 * fold in every logit of a tile.)
+          // The integer sum s (|s| < 2^21) is accumulated onto the bits of
+          // PF_BIAS = 1.5 * 2^23: the result's bits are those of the float
+          // PF_BIAS + s, exactly (ulp 1 on [2^23, 2^24)), with no conversion.
+          // The bias leaves the exp2 argument exactly (see the fold below).
           // Each element passes an empty asm first: reading elements of an
           // int MFMA result one by one otherwise makes this compiler read
           // element 0 for all four.
-          v4i acc = v4i{0, 0, 0, 0};
+          v4i acc = v4i{PF_BIAS_BITS, PF_BIAS_BITS, PF_BIAS_BITS, PF_BIAS_BITS};
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qop[qb][0], acc, 0, 0, 0);
           if constexpr (QB == 32) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb2, qop[qb][1], acc, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             int bits = acc[r];
             asm("" : "+v"(bits));
-            s[kb][qb][r] = (float)bits;
+            s[kb][qb][r] = __builtin_bit_cast(float, bits);
           }
         } else {
           const v8i kop = v8i{ka[0], ka[1], ka[2], ka[3], kb2[0], kb2[1], kb2[2], kb2[3]};
@@ -678,14 +685,39 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
       fold = base_fold * k_sc_blk[kt >> 1];
     else
       fold = base_fold * k_sc_head;
+    // int8: the scores are PF_BIAS + s.  The fold is rounded to 22
+    // significant bits (a change below fp32's own rounding of the scale
+    // product), so that bfold = PF_BIAS * fold is exact and a multiple of
+    // 2^grid_t.  While every reference m_ref is a multiple of 2^m_grid with
+    // m_grid >= grid_t, bfold + m_ref is exact too, and
+    // fma(PF_BIAS + s, fold, -(bfold + m_ref)) is s * fold - m_ref rounded
+    // once: the exp2 argument of an unbiased score.
+    float bfold = 0.0f;
+    int grid_t = -125;
+    bool big = false;   // a grid above 1 would shift p too far: no bias
+    if constexpr (QK_I8) {
+      const uint32_t fb = (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, fold)) + 2u) & ~3u;
+      fold = __builtin_bit_cast(float, fb);
+      bfold = PF_BIAS * fold;
+      grid_t = max((int)((fb >> 23) & 0xffu) - 126, -125);
+      big = grid_t > 0;
+    }
 
-    // ---- mask (only tiles that cross the causal diagonal or the sequence
-    // end): the fold is applied first and the scaled logit of a key past the
-    // row's limit becomes -inf by select, so the mask holds for any fold
+    // ---- mask (tiles that cross the causal diagonal or the sequence end):
+    // the fold is applied first and the scaled logit of a key past the row's
+    // limit becomes -inf by select, so the mask holds for any fold
     // (sm_scale <= 0, scales of either sign) and NaN garbage in a masked key
-    // cannot leak.  Such a tile then continues with a unit fold.
+    // cannot leak.  Such a tile then continues with a unit fold and no bias.
+    // An int8 tile whose fold is too large for the bias grid takes the bias
+    // off instead (same loop, nothing masked) and keeps its fold.
     const bool need_mask = kfirst + PF_BN > min(Lk, wq0 + off + 1);
-    if (need_mask) {
+    if (need_mask || big) {
+      // masked: s * fold or -inf, then a unit fold.  Large fold, no key
+      // masked: PF_BIAS + s - PF_BIAS = s exactly (the two lie within a
+      // factor 2 of each other), and the tile keeps its fold, so its exp2
+      // argument is still s * fold - m_ref rounded once.
+      const float fm = need_mask ? fold : 1.0f;
+      const float bm = need_mask ? bfold : PF_BIAS;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -693,9 +725,17 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kfirst + kb * 16 + 4 * g + r;
-            s[kb][qb][r] = key < lim[qb] ? s[kb][qb][r] * fold : -INFINITY;
+            s[kb][qb][r] = key < lim[qb] ? __builtin_fmaf(s[kb][qb][r], fm, -bm) : -INFINITY;
           }
-      fold = 1.0f;
+      if (need_mask) fold = 1.0f;
+      bfold = 0.0f;
+    }
+    // a biased tile whose fold needs a coarser reference grid than the rows'
+    // references are on goes through the exact path, which moves them up to it
+    bool bump = false;
+    if (QK_I8 && !need_mask && !big && grid_t > m_grid) {
+      m_grid = grid_t;
+      bump = true;
     }
 
     // ---- online softmax against a lagging reference max.  Common path:
@@ -707,7 +747,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
     float lt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float neg_m = -m_ref[qb];
+      const float neg_m = -(bfold + m_ref[qb]);
       lt[qb] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -723,7 +763,7 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
     }
     // NaN-safe: !(x <= bound) also catches inf/NaN partial sums
     const bool redo = !(lt[0] <= PF_TILE_SUM_MAX) || !(lt[1] <= PF_TILE_SUM_MAX);
-    if (__ballot(redo)) {
+    if (__ballot(redo) || bump) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         // the row's largest scaled logit in this tile (masked keys are -inf)
@@ -731,16 +771,22 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) m = fmaxf(m, s[kb][qb][r] * fold);
+          for (int r = 0; r < 4; ++r) m = fmaxf(m, __builtin_fmaf(s[kb][qb][r], fold, -bfold));
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float m_new = fmaxf(m_ref[qb], m);
+        float m_new = fmaxf(m_ref[qb], m);
+        if constexpr (QK_I8) {
+          // up to the next multiple of 2^m_grid (a float at or above 2^23 of
+          // them already is one; -inf stays)
+          const float t = __builtin_ldexpf(m_new, -m_grid);
+          if (fabsf(t) < 0x1p23f) m_new = __builtin_ldexpf(__builtin_ceilf(t), m_grid);
+        }
         const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) oacc[db][qb] *= alpha;
-        const float neg_m = m_new == -INFINITY ? 0.0f : -m_new;
+        const float neg_m = m_new == -INFINITY ? -bfold : -(bfold + m_new);
         lt[qb] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
