@@ -686,10 +686,10 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
     else
       fold = base_fold * k_sc_head;
     // int8: the scores are PF_BIAS + s.  The fold is rounded to 22
-    // significant bits (a change below fp32's own rounding of the scale
-    // product), so that bfold = PF_BIAS * fold is exact and a multiple of
-    // 2^grid_t.  While every reference m_ref is a multiple of 2^m_grid with
-    // m_grid >= grid_t, bfold + m_ref is exact too, and
+    // significant bits (a relative change of at most 2^-23, twice fp32's own
+    // rounding of the scale product), so that bfold = PF_BIAS * fold is exact
+    // and a multiple of 2^grid_t.  While every reference m_ref is a multiple
+    // of 2^m_grid with m_grid >= grid_t, bfold + m_ref is exact too, and
     // fma(PF_BIAS + s, fold, -(bfold + m_ref)) is s * fold - m_ref rounded
     // once: the exp2 argument of an unbiased score.
     float bfold = 0.0f;
