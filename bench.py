@@ -809,7 +809,7 @@ def main():
             print(f"{k}: {v}")
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     import torch
