@@ -469,11 +469,12 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
   // 16-lane group g, lane 4k + q names row 4g + k (+ 16h + 32ks) and the 4
   // values of d = 16db + 4q..; lane n receives d = 16db + n of those 4 rows:
   // keys 32ks + 16h + 4g + 0..3, the keys of P slots 4h..4h+3 of the lane.
+  // Chunk 2db + q/2 of the row sits at (2db + q/2) ^ t, t = tsw(row), i.e.
+  // at 2(db ^ t/2) + (q/2 ^ t%2): the block part is db ^ t/2 in bits 5 and up
+  // of the offset, below the row's, so block db's offset is vtr0 ^ 32db.
   const int vtr_row = 4 * g + (n >> 2), vtr_q = n & 3;
-  int vtr[D / 16];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    vtr[db] = vtr_row * (2 * D) + (((2 * db + (vtr_q >> 1)) ^ G::tsw(vtr_row)) * 16) + (vtr_q & 1) * 8;
+  const int vtr_t = G::tsw(vtr_row);
+  const int vtr0 = vtr_row * (2 * D) + (vtr_t >> 1) * 32 + (((vtr_q >> 1) ^ (vtr_t & 1)) * 16) + (vtr_q & 1) * 8;
 
   // ---- accumulators
   v4f oacc[D / 16][2];
@@ -665,8 +666,9 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
       if constexpr (PAGED) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x2 lo = pf_read_tr16(sv + vtr[db] + (32 * ks) * (2 * D));
-          const u32x2 hi = pf_read_tr16(sv + vtr[db] + (32 * ks + 16) * (2 * D));
+          const int vtr = vtr0 ^ (32 * db);
+          const u32x2 lo = pf_read_tr16(sv + vtr + (32 * ks) * (2 * D));
+          const u32x2 hi = pf_read_tr16(sv + vtr + (32 * ks + 16) * (2 * D));
           dst[ks] = __builtin_bit_cast(v8h, u32x4{lo[0], lo[1], hi[0], hi[1]});
         }
       } else {
