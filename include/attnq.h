@@ -190,7 +190,10 @@ int attn_append_kv_rope(void* q, void* k, const void* v, int dtype, const int32_
  *     sum_d |q_d k_d|, which moves large logits -- outlier-heavy rows -- by more
  *     than the output tolerance allows), or
  *     qk_dtype INT8 with scale_mode INT8_PER_BLOCK (q_scale [B, Hq, ceil(max_seqlen_q/128)],
- *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk), or
+ *     k_scale [B, Hkv, ceil(max_seqlen_k/128)], as written by attn_quant_qk): the
+ *     integer dot products are exact and each tile's multiplier sm_scale * log2(e) *
+ *     q scale * k block scale is carried to 22 significant bits (2^-23 relative, felt
+ *     only by logits of ~1e4 and more), or
  *     qk_dtype BF16 / FP16 with scale_mode INT8_PER_BLOCK_RAW_Q: q is the unquantized
  *     16-bit tensor of that type and k the int8 codes with k_scale as above.  Each
  *     128-query block (counted from its sequence's start) is quantized inside the
