@@ -50,7 +50,10 @@ constexpr int MLA_CPR = MLA_ROW / 16;            // 41 16-byte chunks per row
 constexpr int MLA_RAW = (MLA_STEP * MLA_CPR + MLA_THREADS - 1) / MLA_THREADS;  // 2
 constexpr int NAT_ROW = MLA_NOPE + 16;           // bf16 per token row: 1056 B, 8 banks apart
 constexpr int ROPE_ROW = MLA_ROPE + 8;           // bf16 per rope row
+constexpr int XROW = MLA_STEP + 4;               // floats per head row of the score / P exchange (36 banks apart)
 constexpr int MLA_SPLIT_TOKENS = 512;            // indices per split (16 steps)
+constexpr int MLA_BT_LDS = 2048;                 // block-table rows up to this long are read into LDS
+static_assert(MLA_THREADS >= MLA_SPLIT_TOKENS, "one slot per thread");
 constexpr float MLA_LN2 = 0.69314718055994530942f;
 // a step whose partial row sum stays at or below this keeps the lagging
 // reference max (every p <= 2^14)
@@ -59,14 +62,18 @@ constexpr float MLA_TILE_SUM_MAX = 16384.0f;
 struct MlaStage {
   uint16_t nat[MLA_STEP * NAT_ROW];  // bf16 codes
   uint16_t rope[MLA_STEP * ROPE_ROW];
-  float scale[MLA_STEP * 4];
+  float scale[4][MLA_STEP];          // [tile][token]
 };
 constexpr int MLA_NBUF = 2;  // staging buffers: step st computes, step st + 1 is staged
 struct MlaLds {
   MlaStage buf[MLA_NBUF];
-  v4f xs[4][2][4][64];            // partial scores [head block][16-token block][channel tile][lane]
+  float part[4][4][16][XROW];     // partial scores [head block][channel tile][head][token]
+  float pex[4][16][XROW];         // P [head block][head][token]
+  float alpha[4][16];             // this step's rescale of O per head (1 unless the reference moved)
+  float lsum[4][16];              // row sums of the split per head
   int row_idx[MLA_SPLIT_TOKENS];  // cache row of each selected index, -1 if unused
   float mask[MLA_SPLIT_TOKENS];   // 0 for a used slot, -inf otherwise (added to its logits)
+  int bt[MLA_BT_LDS];             // the sequence's block-table row, when it fits
 };
 
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -81,13 +88,12 @@ ATTNQ_DEV uint2 read_tr16(const uint16_t* p) {
 }
 
 // 4 int8 codes -> 4 bf16 values, exactly (|code| <= 128 has at most 8
-// significant bits): each byte converted to fp32, pairs rounded to bf16.
+// significant bits): each signed byte converted to fp32 (one instruction per
+// byte with a sign-extending byte select), pairs packed by taking the upper
+// halves, which are the exact bf16 patterns.
 ATTNQ_DEV void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  // code + 128 as unsigned bytes, each converted exactly to fp32, minus 128;
-  // the upper halves of the fp32 values are the exact bf16 patterns
-  const uint32_t u = w ^ 0x80808080u;
-  const float f0 = (float)(u & 0xffu) - 128.0f, f1 = (float)((u >> 8) & 0xffu) - 128.0f;
-  const float f2 = (float)((u >> 16) & 0xffu) - 128.0f, f3 = (float)(u >> 24) - 128.0f;
+  const float f0 = (float)(int8_t)(w), f1 = (float)(int8_t)(w >> 8);
+  const float f2 = (float)(int8_t)(w >> 16), f3 = (float)((int32_t)w >> 24);
   lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hb = wave & 3;  // 16-head block
-  const int t = wave >> 2;  // 128-channel tile of QK and PV (t = 3 also owns rope)
+  const int t = wave >> 2;  // 128-channel tile of QK and PV (t = 3 also owns rope); softmax of heads 4t..4t+3
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, row = blockIdx.y;  // row = b * s_q + s
   const int b = row / a.s_q;
@@ -114,30 +120,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
   const int e_end = min(ntok, e_begin + MLA_SPLIT_TOKENS);
   const int head = blockIdx.z * MLA_WG_HEADS + hb * 16 + n;
   const bool wave_active = blockIdx.z * MLA_WG_HEADS + hb * 16 < a.heads;
-
-  // ---- resolve this split's token slots to cache rows once.  Slot u is
-  // token idx[u / sbs] * sbs + u % sbs; used below `lim`.
-  {
-    const int kv_len = a.kv_lens[b];
-    const int s = row - b * a.s_q;
-    const int lim = md.sparse_mode == 3 ? kv_len - a.s_q + s + 1 : kv_len;
-    const int sh = __builtin_ctz((unsigned)sbs);
-    const int* idx_row = a.idx + (long)row * a.topk;
-    for (int e = threadIdx.x; e < MLA_SPLIT_TOKENS; e += MLA_THREADS) {
-      int r = -1;
-      const int u = e_begin + e;
-      if (u < e_end) {
-        const int ent = idx_row[u >> sh];
-        const long i = ((long)ent << sh) + (u & (sbs - 1));
-        if (ent >= 0 && i < lim && i / a.block_size < a.max_blocks) {
-          const int blk = a.block_table[(long)b * a.max_blocks + (int)(i / a.block_size)];
-          if (blk >= 0 && blk < a.num_blocks) r = blk * a.block_size + (int)(i % a.block_size);
-        }
-      }
-      L.row_idx[e] = r;
-      L.mask[e] = r >= 0 ? 0.0f : -INFINITY;
-    }
-  }
+  // softmax lanes: head sh of the block (4t + lane / 16), tokens 2 (lane % 16) + {0, 1}
+  const int sh = 4 * t + (lane >> 4), sk = 2 * (lane & 15);
 
   // ---- query operands (bf16, as given) of this wave's nope tile and, for t = 3, rope
   v8bf qn[4];
@@ -157,27 +141,60 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       qr[m] = __builtin_bit_cast(v8bf, w);
     }
   }
+  // ---- resolve this split's token slots to cache rows once.  Slot u is
+  // token idx[u / sbs] * sbs + u % sbs; used below `lim`.  The sequence's
+  // block-table row is read into LDS beside the index loads when it fits,
+  // so the lookup costs no second dependent round trip to memory.
+  {
+    const int kv_len = a.kv_lens[b];
+    const int s = row - b * a.s_q;
+    const int lim = md.sparse_mode == 3 ? kv_len - a.s_q + s + 1 : kv_len;
+    const int sbl = __builtin_ctz((unsigned)sbs);
+    const int* idx_row = a.idx + (long)row * a.topk;
+    const int* bt_row = a.block_table + (long)b * a.max_blocks;
+    const bool bt_lds = a.max_blocks <= MLA_BT_LDS;
+    if (bt_lds)
+      for (int i = threadIdx.x; i < a.max_blocks; i += MLA_THREADS) L.bt[i] = bt_row[i];
+    const int e = threadIdx.x;  // one slot per thread (MLA_THREADS >= MLA_SPLIT_TOKENS)
+    const int u = e_begin + e;
+    const int ent = (e < MLA_SPLIT_TOKENS && u < e_end) ? idx_row[u >> sbl] : -1;
+    __syncthreads();  // block-table row in LDS
+    if (e < MLA_SPLIT_TOKENS) {
+      int r = -1;
+      const long i = ((long)ent << sbl) + (u & (sbs - 1));
+      if (ent >= 0 && i < lim && i / a.block_size < a.max_blocks) {
+        const int bi = (int)(i / a.block_size);
+        const int blk = bt_lds ? L.bt[bi] : bt_row[bi];
+        if (blk >= 0 && blk < a.num_blocks) r = blk * a.block_size + (int)(i % a.block_size);
+      }
+      L.row_idx[e] = r;
+      L.mask[e] = r >= 0 ? 0.0f : -INFINITY;
+    }
+  }
   __syncthreads();  // row_idx visible
 
-  v4f oacc[8];  // O^T for channels [128 t, 128 t + 128)
+  v4f oacc[8];  // O^T for channels [128 t, 128 t + 128), head n
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
-  // reference max (log2 units); -inf until set so the first step's p are
-  // inf/NaN and force the exact path
+  // reference max (log2 units) of head sh; -inf until set so the first
+  // step's p are inf/NaN and force the exact path
   float m_ref = -INFINITY, l_run = 0.f;
 
   // ---- staging: chunk c of a step = (row c % 32, 16-byte column c / 32).
   // The rows of step st + 1 are gathered into registers while step st computes.
   u32x4 raw[MLA_RAW];
   auto gather = [&](int st) {
+    int rr[MLA_RAW];
+    static_for<0, MLA_RAW>([&](auto ki) {
+      constexpr int k = decltype(ki)::value;
+      const int c = threadIdx.x + k * MLA_THREADS;
+      rr[k] = c < MLA_STEP * MLA_CPR ? L.row_idx[st * MLA_STEP + (c % MLA_STEP)] : -1;
+    });
     static_for<0, MLA_RAW>([&](auto ki) {
       constexpr int k = decltype(ki)::value;
       const int c = threadIdx.x + k * MLA_THREADS;
       raw[k] = u32x4{0u, 0u, 0u, 0u};
-      if (c < MLA_STEP * MLA_CPR) {
-        const int r = L.row_idx[st * MLA_STEP + (c % MLA_STEP)];
-        if (r >= 0) raw[k] = *reinterpret_cast<const u32x4*>(a.cache + (long)r * MLA_ROW + (c / MLA_STEP) * 16);
-      }
+      if (rr[k] >= 0) raw[k] = *reinterpret_cast<const u32x4*>(a.cache + (long)rr[k] * MLA_ROW + (c / MLA_STEP) * 16);
     });
   };
   auto stage = [&](MlaStage& B) {
@@ -199,16 +216,22 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
         } else if (col < MLA_NOPE + 2 * MLA_ROPE) {
           *reinterpret_cast<u32x4*>(&B.rope[r * ROPE_ROW + (col - MLA_NOPE) / 2]) = raw[k];
         } else {
-          *reinterpret_cast<u32x4*>(&B.scale[r * 4]) = raw[k];  // zero for unused rows
+#pragma unroll
+          for (int u = 0; u < 4; ++u) B.scale[u][r] = __uint_as_float(raw[k][u]);  // zero for unused rows
         }
       }
     });
   };
 
-  // Pipeline: step st computes on buffer st % 2.  Between the two barriers of
-  // step st the workgroup stages step st + 1 (gathered into registers during
-  // step st - 1) into the other buffer -- free because every wave finished
-  // the PV of step st - 1 before the first barrier -- and gathers step st + 2.
+  // Pipeline: step st computes on buffer st % 2.
+  //   QK: each wave's partial S^T (its tile's codes times the tile scales,
+  //   plus rope for t = 3) to LDS -> barrier -> softmax: wave t of a head
+  //   block sums the four partials of heads 4t..4t+3 and computes their P
+  //   and rescale factors (so each value is computed once), to LDS; the
+  //   workgroup stages step st + 1 (gathered during step st - 1) into the
+  //   other buffer -- free because every wave finished the PV of step
+  //   st - 1 before the first barrier -- and gathers step st + 2 ->
+  //   barrier -> PV: every wave rescales its O tile and adds P V.
   const int nsteps = e_end > e_begin ? (e_end - e_begin + MLA_STEP - 1) / MLA_STEP : 0;
   if (nsteps > 0) {
     gather(0);
@@ -218,16 +241,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
   }
   for (int st = 0; st < nsteps; ++st) {
     MlaStage& B = L.buf[st % MLA_NBUF];
-    v4f (*xs)[2][4][64] = L.xs;
-    // ---- partial S^T of this wave's tile, lane (n, g): tokens 16j + 4g + r, head n
-    float sp[2][4];
-    // this lane's tokens' scales of tile t (used by QK and by P)
-    float sc[2][4];
+    // this lane's tokens' scales of tile t: tokens 16j + 4g + r
+    v4f sc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[j][r] = B.scale[(16 * j + 4 * g + r) * 4 + t];
+    for (int j = 0; j < 2; ++j) sc[j] = *reinterpret_cast<const v4f*>(&B.scale[t][16 * j + 4 * g]);
     if (wave_active) {
+      // ---- partial S^T of this wave's tile, lane (n, g): tokens 16j + 4g + r, head n
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -236,8 +255,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
           const v8bf kop = *reinterpret_cast<const v8bf*>(&B.nat[(16 * j + n) * NAT_ROW + 128 * t + 32 * g + 8 * m]);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qn[m], acc, 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sp[j][r] = sc[j][r] * acc[r];
+        v4f sp = sc[j] * acc;
         if (t == 3) {
           v4f racc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -245,79 +263,69 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
             const v8bf kop = *reinterpret_cast<const v8bf*>(&B.rope[(16 * j + n) * ROPE_ROW + 16 * g + 8 * m]);
             racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[m], racc, 0, 0, 0);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sp[j][r] += racc[r];
+          sp += racc;
         }
-        xs[hb][j][t][lane] = v4f{sp[j][0], sp[j][1], sp[j][2], sp[j][3]};
+        *reinterpret_cast<v4f*>(&L.part[hb][t][n][16 * j + 4 * g]) = sp;
       }
     }
-    __syncthreads();  // scores exchanged; the PV of step st - 1 is done everywhere
+    __syncthreads();  // partial scores exchanged; the PV of step st - 1 is done everywhere
+    if (wave_active) {
+      // ---- logits of head sh, tokens sk, sk + 1: the mask adds -inf to an
+      // unused slot, whose staged row (codes, scales, rope) is all zeros, so
+      // its score is 0 and the sum -inf for any sm_scale
+      v2f x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const v2f*>(&L.part[hb][u][sh][sk]);
+      const v2f tot = (x[0] + x[1]) + (x[2] + x[3]);
+      const v2f mk = *reinterpret_cast<const v2f*>(&L.mask[st * MLA_STEP + sk]);
+      const float s0 = __builtin_fmaf(tot[0], a.sm_scale_log2, mk[0]);
+      const float s1 = __builtin_fmaf(tot[1], a.sm_scale_log2, mk[1]);
+      // ---- softmax against a lagging reference max; exact path when a step
+      // would leave the bound or no reference exists yet
+      float p0 = __builtin_amdgcn_exp2f(s0 - m_ref), p1 = __builtin_amdgcn_exp2f(s1 - m_ref);
+      float lt = p0 + p1;
+      float al = 1.0f;
+      if (__ballot(!(lt <= MLA_TILE_SUM_MAX))) {
+        float mx = fmaxf(s0, s1);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const float m_new = fmaxf(m_ref, mx);
+        al = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= al;
+        const float mu = m_new == -INFINITY ? 0.0f : m_new;
+        p0 = __builtin_amdgcn_exp2f(s0 - mu);
+        p1 = __builtin_amdgcn_exp2f(s1 - mu);
+        lt = p0 + p1;
+      }
+      l_run += lt;
+      *reinterpret_cast<v2f*>(&L.pex[hb][sh][sk]) = v2f{p0, p1};
+      if ((lane & 15) == 0) L.alpha[hb][sh] = al;
+    }
     // stage step st + 1 (gathered during step st - 1), gather step st + 2
     if (st + 1 < nsteps) stage(L.buf[(st + 1) % MLA_NBUF]);
     if (st + 2 < nsteps) gather(st + 2);
-    if (!wave_active) {
-      __syncthreads();
-      continue;
-    }
-    // logits of the lane's tokens 16j + 4g + r: the mask adds -inf to an
-    // unused slot, whose staged row (codes, scales, rope) is all zeros, so
-    // its score is 0 and the sum -inf for any sm_scale
-    float s[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const v4f tot = (xs[hb][j][0][lane] + xs[hb][j][1][lane]) + (xs[hb][j][2][lane] + xs[hb][j][3][lane]);
-      const float* mk = &L.mask[st * MLA_STEP + 16 * j + 4 * g];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[j][r] = __builtin_fmaf(tot[r], a.sm_scale_log2, mk[r]);
-    }
-
-    // ---- softmax against a lagging reference max (the four waves of a
-    // head block compute identical values); exact path when a step would
-    // leave fp16 range or no reference exists yet
-    float p[8];
-    float lt = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < 8; sl += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4] - m_ref);
-      const float p1 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4 + 1] - m_ref);
-      p[sl] = p0;
-      p[sl + 1] = p1;
-      lt += p0 + p1;
-    }
-    if (__ballot(!(lt <= MLA_TILE_SUM_MAX))) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) mx = fmaxf(mx, s[sl / 4][sl % 4]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
-      const float mu = m_new == -INFINITY ? 0.0f : m_new;
-      lt = 0.f;
-#pragma unroll
-      for (int sl = 0; sl < 8; sl += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4] - mu);
-        const float p1 = __builtin_amdgcn_exp2f(s[sl / 4][sl % 4 + 1] - mu);
-        p[sl] = p0;
-        p[sl + 1] = p1;
-        lt += p0 + p1;
-      }
-    }
-    l_run += lt;
+    __syncthreads();  // P and rescale factors exchanged; step st + 1 staged
+    if (!wave_active) continue;
 
     // ---- O^T += codes^T (P * scale_t)^T for this wave's tile.  Slot sl of
     // lane group g is token (sl / 4) * 16 + 4g + sl % 4; the codes^T operand
     // comes from the token-major rows through two transposed reads.
+    const float al = L.alpha[hb][n];
+    if (__ballot(al != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= al;
+    }
     v8bf pk;
 #pragma unroll
-    for (int sl = 0; sl < 8; sl += 2) {
-      const v2bf pb = __builtin_convertvector(v2f{p[sl] * sc[sl / 4][sl % 4], p[sl + 1] * sc[sl / 4][sl % 4 + 1]}, v2bf);
-      pk[sl] = pb[0];
-      pk[sl + 1] = pb[1];
+    for (int j = 0; j < 2; ++j) {
+      const v4f pw = *reinterpret_cast<const v4f*>(&L.pex[hb][n][16 * j + 4 * g]) * sc[j];
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const v2bf pb = __builtin_convertvector(v2f{pw[r], pw[r + 1]}, v2bf);
+        pk[4 * j + r] = pb[0];
+        pk[4 * j + r + 1] = pb[1];
+      }
     }
     // address lane (g, 4k + q) names token (4g + k) (+16), channels 4q..4q+3 of the d-block
     const int tr_row = 4 * g + (n >> 2), tr_col = 4 * (n & 3);
@@ -329,60 +337,105 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       const v8bf vop = __builtin_bit_cast(v8bf, u32x4{lo.x, lo.y, hi.x, hi.y});
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pk, oacc[db], 0, 0, 0);
     }
-    __syncthreads();  // step st + 1 staged; exchange buffer free again
   }
-  if (!wave_active) return;
   // ---- partial result of this split: normalized O and log2-sum-exp
-  float l = l_run;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (head < a.heads) {
-    const long prow = ((long)row * a.n_split + split) * a.heads + head;
-    const float inv = l != 0.f ? 1.f / l : 0.f;  // a NaN sum stays NaN
+  if (wave_active) {
+    float l = l_run;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const v4f o4 = oacc[db] * inv;
-      const uint32_t w0 = f32_to_bf16(o4[0]) | (f32_to_bf16(o4[1]) << 16);
-      const uint32_t w1 = f32_to_bf16(o4[2]) | (f32_to_bf16(o4[3]) << 16);
-      *reinterpret_cast<uint2*>(a.ws_o + prow * MLA_NOPE + 128 * t + db * 16 + 4 * g) = make_uint2(w0, w1);
+    for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+    if ((lane & 15) == 0) {
+      L.lsum[hb][sh] = l;
+      const int hs = blockIdx.z * MLA_WG_HEADS + hb * 16 + sh;
+      if (hs < a.heads) a.ws_lse[((long)row * a.n_split + split) * a.heads + hs] = l != 0.f ? m_ref + __log2f(l) : -INFINITY;
     }
-    if (g == 0 && t == 0) a.ws_lse[prow] = l != 0.f ? m_ref + __log2f(l) : -INFINITY;
+  }
+  __syncthreads();  // row sums visible
+  if (!wave_active || head >= a.heads) return;
+  const float l = L.lsum[hb][n];
+  const long prow = ((long)row * a.n_split + split) * a.heads + head;
+  const float inv = l != 0.f ? 1.f / l : 0.f;  // a NaN sum stays NaN
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const v4f o4 = oacc[db] * inv;
+    const uint32_t w0 = f32_to_bf16(o4[0]) | (f32_to_bf16(o4[1]) << 16);
+    const uint32_t w1 = f32_to_bf16(o4[2]) | (f32_to_bf16(o4[3]) << 16);
+    *reinterpret_cast<uint2*>(a.ws_o + prow * MLA_NOPE + 128 * t + db * 16 + 4 * g) = make_uint2(w0, w1);
   }
 }
 
-// Merge of the splits: one 128-thread workgroup per (query row, head).
-__global__ __launch_bounds__(128) void k_mla_merge(const MlaArgs a) {
-  const int rh = blockIdx.x;  // row * heads + head
-  const int row = rh / a.heads, head = rh % a.heads;
-  const int d0 = threadIdx.x * 4;
+// Merge of the splits: one 256-thread workgroup per (query row, 8 heads),
+// 32 threads per head, 16 channels per thread.  The first four splits' lse
+// and partials are loaded together, then the maximum is taken over all
+// splits; a split whose lse is -inf (no used token with p > 0) is skipped.
+constexpr int MRG_HEADS = 8;
+constexpr int MRG_CHUNK = 4;
+__global__ __launch_bounds__(256) void k_mla_merge(const MlaArgs a) {
+  const int hgs = (a.heads + MRG_HEADS - 1) / MRG_HEADS;
+  const int row = blockIdx.x / hgs;
+  const int head = (blockIdx.x - row * hgs) * MRG_HEADS + (threadIdx.x >> 5);
+  if (head >= a.heads) return;
+  const int d0 = (threadIdx.x & 31) * 16;
+  const long base = (long)row * a.n_split * a.heads + head;  // partial row of split c: base + c * heads
+  float lc[MRG_CHUNK];
+  u32x4 v[MRG_CHUNK][2];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < MRG_CHUNK; ++k) {
+      const int c = c0 + k;
+      lc[k] = -INFINITY;
+      if (c < a.n_split) {
+        const long prow = base + (long)c * a.heads;
+        lc[k] = a.ws_lse[prow];
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.ws_o + prow * MLA_NOPE + d0);
+        v[k][0] = src[0];
+        v[k][1] = src[1];
+      }
+    }
+  };
+  load_chunk(0);
   // a NaN partial (a NaN value among the used tokens) makes the row NaN
   float m = -INFINITY;
   bool nan = false;
-  for (int c = 0; c < a.n_split; ++c) {
-    const float lc = a.ws_lse[((long)row * a.n_split + c) * a.heads + head];
-    nan |= lc != lc;
-    m = fmaxf(m, lc);
+#pragma unroll
+  for (int k = 0; k < MRG_CHUNK; ++k) {
+    nan |= lc[k] != lc[k];
+    m = fmaxf(m, lc[k]);
   }
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = MRG_CHUNK; c < a.n_split; ++c) {
+    const float x = a.ws_lse[base + (long)c * a.heads];
+    nan |= x != x;
+    m = fmaxf(m, x);
+  }
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   float tot = 0.f;
   if (m != -INFINITY && !nan) {
-    for (int c = 0; c < a.n_split; ++c) {
-      const long prow = ((long)row * a.n_split + c) * a.heads + head;
-      const float lc = a.ws_lse[prow];
-      if (lc == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(lc - m);
-      tot += w;
-      const uint2 o2 = *reinterpret_cast<const uint2*>(a.ws_o + prow * MLA_NOPE + d0);
-      acc[0] += w * bf16_to_f32(o2.x & 0xffffu); acc[1] += w * bf16_to_f32(o2.x >> 16);
-      acc[2] += w * bf16_to_f32(o2.y & 0xffffu); acc[3] += w * bf16_to_f32(o2.y >> 16);
+    for (int c0 = 0; c0 < a.n_split; c0 += MRG_CHUNK) {
+      if (c0 > 0) load_chunk(c0);
+#pragma unroll
+      for (int k = 0; k < MRG_CHUNK; ++k) {
+        if (lc[k] == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(lc[k] - m);
+        tot += w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t x = v[k][i >> 2][i & 3];
+          acc[2 * i] += w * bf16_to_f32(x & 0xffffu);
+          acc[2 * i + 1] += w * bf16_to_f32(x >> 16);
+        }
+      }
     }
   }
   const float inv = nan ? __builtin_nanf("") : tot > 0.f ? 1.f / tot : 0.f;
-  uint32_t w0 = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
-  uint32_t w1 = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + (long)rh * MLA_NOPE + d0) = make_uint2(w0, w1);
-  if (a.lse && threadIdx.x == 0)
-    a.lse[rh] = nan ? __builtin_nanf("") : tot > 0.f ? (m + __log2f(tot)) * MLA_LN2 : -INFINITY;
+  u32x4 out[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i >> 2][i & 3] = f32_to_bf16(acc[2 * i] * inv) | (f32_to_bf16(acc[2 * i + 1] * inv) << 16);
+  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + ((long)row * a.heads + head) * MLA_NOPE + d0);
+  dst[0] = out[0];
+  dst[1] = out[1];
+  if (a.lse && (threadIdx.x & 31) == 0)
+    a.lse[(long)row * a.heads + head] = nan ? __builtin_nanf("") : tot > 0.f ? (m + __log2f(tot)) * MLA_LN2 : -INFINITY;
 }
 
 int mla_n_split(int topk) { return (topk + MLA_SPLIT_TOKENS - 1) / MLA_SPLIT_TOKENS; }
@@ -401,7 +454,7 @@ bool launch_mla_mode(const MlaArgs& a, const MlaMode& m, hipStream_t s) {
   else
     hipLaunchKernelGGL((k_mla_split<false>), dim3(a.n_split, rows, hgroups), dim3(MLA_THREADS), 0, s, a, m);
   if (hipGetLastError() != hipSuccess) return false;
-  hipLaunchKernelGGL(k_mla_merge, dim3(rows * a.heads), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(k_mla_merge, dim3(rows * ((a.heads + MRG_HEADS - 1) / MRG_HEADS)), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess;
 }
 
