@@ -11,19 +11,24 @@
 //
 // Split phase: one workgroup (16 waves) per (query row, 512-index split,
 // group of 64 heads).  The split's indices are resolved through block_table
-// once, into LDS.  Per 32-index step the workgroup gathers the 32 selected
-// rows and widens the codes to bf16 (exact for int8 and e4m3fn) into
-// token-major LDS rows.  Four waves serve 16 heads, split by channel tile:
-// each owns one 128-channel tile of QK and PV (the last one also the rope
-// part) and the four exchange their partial scores through LDS once per
-// step; the PV operand (channel-major) is read from the token-major rows
-// with transposing LDS reads:
+// once, into LDS (the block-table row itself is read into LDS beside the
+// index loads when it holds at most 2048 entries).  Per 32-index step the
+// workgroup gathers the 32 selected rows and widens the codes to bf16
+// (exact for int8 and e4m3fn) into token-major LDS rows.  Four waves serve
+// 16 heads, split by channel tile: each owns one 128-channel tile of QK and
+// PV (the last one also the rope part):
 //   S^T = K Q^T    per 128-channel tile: bf16 16x16x32 MFMA on the exact
 //                  codes and the bf16 query, then the tile's scale per token
-//                  in fp32; rope part: bf16 MFMA;
-//   softmax per head against a lagging reference max (exact rescale only
-//   when a step's row sum leaves [0, 2^14]), lane-local partial sums;
-//   O^T += codes^T (P * scale_t)^T   bf16 MFMA, one P operand per tile.
+//                  in fp32; rope part: bf16 MFMA; the partial scores go to
+//                  LDS;
+//   softmax: wave t of a head block sums the four partials of heads
+//                  4t..4t+3 (each score and each P is computed once), against
+//                  a lagging reference max per head (exact rescale only when
+//                  a lane's two p leave [0, 2^14]), and publishes P and the
+//                  step's rescale factor of O per head;
+//   O^T += codes^T (P * scale_t)^T   bf16 MFMA, one P operand per tile; the
+//                  PV operand (channel-major) is read from the token-major
+//                  rows with transposing LDS reads.
 // P * scale_t is rounded to bf16, whose range is fp32's: with p <= 2^14 the
 // operand stays finite for every tile scale up to 2^100 in magnitude.
 // Each split writes its normalized partial O (bf16) and log2-sum-exp; the
