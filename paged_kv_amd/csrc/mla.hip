@@ -65,7 +65,7 @@ constexpr float MLA_LN2 = 0.69314718055994530942f;
 constexpr float MLA_TILE_SUM_MAX = 16384.0f;
 
 struct MlaStage {
-  uint16_t nat[MLA_STEP * NAT_ROW];  // bf16 codes
+  uint16_t nat[MLA_STEP * NAT_ROW + 8];  // bf16 codes, row r at nat_row(r)
   uint16_t rope[MLA_STEP * ROPE_ROW];
   float scale[4][MLA_STEP];          // [tile][token]
 };
@@ -80,6 +80,13 @@ struct MlaLds {
   float mask[MLA_SPLIT_TOKENS];   // 0 for a used slot, -inf otherwise (added to its logits)
   int bt[MLA_BT_LDS];             // the sequence's block-table row, when it fits
 };
+
+// LDS serves 16-byte reads and writes 32 lanes per pass across 128 4-byte
+// banks.  Rows of staged codes are 264 banks apart and rows 16..31 sit 4
+// banks further on, so the 32 rows of a staging write, the 16 rows x 2
+// channel groups of a K-operand read and the 16 rows x 32 bytes of a
+// transposed read each hit distinct banks.
+ATTNQ_DEV int nat_row(int r) { return r * NAT_ROW + 8 * (r >> 4); }
 
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) lds_h4* lds_h4_ptr;
@@ -136,12 +143,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long)row * a.heads + head) * (MLA_NOPE + MLA_ROPE);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 128 * t + 32 * g + 8 * m) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 w = have ? *reinterpret_cast<const u32x4*>(qp + 128 * t + 8 * g + 32 * m) : u32x4{0u, 0u, 0u, 0u};
       qn[m] = __builtin_bit_cast(v8bf, w);
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const u32x4 w = (have && t == 3) ? *reinterpret_cast<const u32x4*>(qp + MLA_NOPE + 16 * g + 8 * m)
+      const u32x4 w = (have && t == 3) ? *reinterpret_cast<const u32x4*>(qp + MLA_NOPE + 8 * g + 32 * m)
                                        : u32x4{0u, 0u, 0u, 0u};
       qr[m] = __builtin_bit_cast(v8bf, w);
     }
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
             if constexpr (KV_FP8) f8x4_to_bf16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
             else i8x4_to_bf16x4(raw[k][e], h[2 * e], h[2 * e + 1]);
           }
-          u32x4* dn = reinterpret_cast<u32x4*>(&B.nat[r * NAT_ROW + col]);
+          u32x4* dn = reinterpret_cast<u32x4*>(&B.nat[nat_row(r) + col]);
           dn[0] = u32x4{h[0], h[1], h[2], h[3]};
           dn[1] = u32x4{h[4], h[5], h[6], h[7]};
         } else if (col < MLA_NOPE + 2 * MLA_ROPE) {
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const v8bf kop = *reinterpret_cast<const v8bf*>(&B.nat[(16 * j + n) * NAT_ROW + 128 * t + 32 * g + 8 * m]);
+          const v8bf kop = *reinterpret_cast<const v8bf*>(&B.nat[nat_row(16 * j + n) + 128 * t + 8 * g + 32 * m]);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qn[m], acc, 0, 0, 0);
         }
         v4f sp = sc[j] * acc;
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
           v4f racc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const v8bf kop = *reinterpret_cast<const v8bf*>(&B.rope[(16 * j + n) * ROPE_ROW + 16 * g + 8 * m]);
+            const v8bf kop = *reinterpret_cast<const v8bf*>(&B.rope[(16 * j + n) * ROPE_ROW + 8 * g + 32 * m]);
             racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[m], racc, 0, 0, 0);
           }
           sp += racc;
@@ -337,8 +344,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int c0 = 128 * t + 16 * db + tr_col;
-      const uint2 lo = read_tr16(&B.nat[tr_row * NAT_ROW + c0]);
-      const uint2 hi = read_tr16(&B.nat[(16 + tr_row) * NAT_ROW + c0]);
+      const uint2 lo = read_tr16(&B.nat[nat_row(tr_row) + c0]);
+      const uint2 hi = read_tr16(&B.nat[nat_row(16 + tr_row) + c0]);
       const v8bf vop = __builtin_bit_cast(v8bf, u32x4{lo.x, lo.y, hi.x, hi.y});
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pk, oacc[db], 0, 0, 0);
     }
