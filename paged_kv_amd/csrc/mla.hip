@@ -55,7 +55,6 @@ constexpr int MLA_CPR = MLA_ROW / 16;            // 41 16-byte chunks per row
 constexpr int MLA_RAW = (MLA_STEP * MLA_CPR + MLA_THREADS - 1) / MLA_THREADS;  // 2
 constexpr int NAT_ROW = MLA_NOPE + 16;           // bf16 per token row: 1056 B, 8 banks apart
 constexpr int ROPE_ROW = MLA_ROPE + 8;           // bf16 per rope row
-constexpr int XROW = MLA_STEP + 4;               // floats per head row of the score / P exchange (36 banks apart)
 constexpr int MLA_SPLIT_TOKENS = 512;            // indices per split (16 steps)
 constexpr int MLA_BT_LDS = 2048;                 // block-table rows up to this long are read into LDS
 static_assert(MLA_THREADS >= MLA_SPLIT_TOKENS, "one slot per thread");
@@ -72,8 +71,8 @@ struct MlaStage {
 constexpr int MLA_NBUF = 2;  // staging buffers: step st computes, step st + 1 is staged
 struct MlaLds {
   MlaStage buf[MLA_NBUF];
-  float part[4][4][16][XROW];     // partial scores [head block][channel tile][head][token]
-  float pex[4][16][XROW];         // P [head block][head][token]
+  float part[4][4][16 * MLA_STEP];  // partial scores [head block][channel tile][xsw(head, token)]
+  float pex[4][16 * MLA_STEP];      // P [head block][xsw(head, token)]
   float alpha[4][16];             // this step's rescale of O per head (1 unless the reference moved)
   float lsum[4][16];              // row sums of the split per head
   int row_idx[MLA_SPLIT_TOKENS];  // cache row of each selected index, -1 if unused
@@ -81,12 +80,18 @@ struct MlaLds {
   int bt[MLA_BT_LDS];             // the sequence's block-table row, when it fits
 };
 
-// LDS serves 16-byte reads and writes 32 lanes per pass across 128 4-byte
-// banks.  Rows of staged codes are 264 banks apart and rows 16..31 sit 4
-// banks further on, so the 32 rows of a staging write, the 16 rows x 2
-// channel groups of a K-operand read and the 16 rows x 32 bytes of a
-// transposed read each hit distinct banks.
+// LDS serves reads 32 lanes per pass (16-byte) or 64 lanes per pass
+// (8-byte) across 128 4-byte banks, and 16-byte writes 16 lanes per pass
+// across 64 banks.  Rows of staged codes are 264 banks apart and rows 16..31
+// sit 4 banks further on, so the 16 rows x 2 channel groups of a K-operand
+// read and the 16 rows x 32 bytes of a transposed read each hit distinct
+// banks.
 ATTNQ_DEV int nat_row(int r) { return r * NAT_ROW + 8 * (r >> 4); }
+// Offset of (head h, token k) in a 16-head x 32-token exchange array: rows of
+// 32 floats whose 4-token groups are XOR-swizzled by h / 2, so the 16-byte
+// writes and reads of 16 heads x one token group and the 8-byte reads and
+// writes of 4 heads x 32 tokens each hit distinct banks.
+ATTNQ_DEV int xsw(int h, int k) { return h * MLA_STEP + ((((k >> 2) ^ ((h >> 1) & 7)) << 2) | (k & 3)); }
 
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) lds_h4* lds_h4_ptr;
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
           }
           sp += racc;
         }
-        *reinterpret_cast<v4f*>(&L.part[hb][t][n][16 * j + 4 * g]) = sp;
+        *reinterpret_cast<v4f*>(&L.part[hb][t][xsw(n, 16 * j + 4 * g)]) = sp;
       }
     }
     __syncthreads();  // partial scores exchanged; the PV of step st - 1 is done everywhere
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       // its score is 0 and the sum -inf for any sm_scale
       v2f x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const v2f*>(&L.part[hb][u][sh][sk]);
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const v2f*>(&L.part[hb][u][xsw(sh, sk)]);
       const v2f tot = (x[0] + x[1]) + (x[2] + x[3]);
       const v2f mk = *reinterpret_cast<const v2f*>(&L.mask[st * MLA_STEP + sk]);
       const float s0 = __builtin_fmaf(tot[0], a.sm_scale_log2, mk[0]);
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
         lt = p0 + p1;
       }
       l_run += lt;
-      *reinterpret_cast<v2f*>(&L.pex[hb][sh][sk]) = v2f{p0, p1};
+      *reinterpret_cast<v2f*>(&L.pex[hb][xsw(sh, sk)]) = v2f{p0, p1};
       if ((lane & 15) == 0) L.alpha[hb][sh] = al;
     }
     // stage step st + 1 (gathered during step st - 1), gather step st + 2
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
     v8bf pk;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const v4f pw = *reinterpret_cast<const v4f*>(&L.pex[hb][n][16 * j + 4 * g]) * sc[j];
+      const v4f pw = *reinterpret_cast<const v4f*>(&L.pex[hb][xsw(n, 16 * j + 4 * g)]) * sc[j];
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
         const v2bf pb = __builtin_convertvector(v2f{pw[r], pw[r + 1]}, v2bf);
