@@ -77,9 +77,9 @@ constexpr int PF_RSRC_W3 = 0x00020000;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // LDS tile geometry.  Rows are unpadded; the 16-byte chunk c of row r sits at
-// chunk position c ^ swizzle(r), so that the 8 lanes an LDS b128 pass serves
-// (rows n..n+7 of one chunk column) hit 8 distinct bank groups, and the
-// direct loads (64 lanes x 16 contiguous bytes) write linearly.
+// chunk position c ^ swizzle(r), which spreads the rows of one chunk column
+// over the banks (unswizzled rows read at half the rate), while the direct
+// loads (64 lanes x 16 contiguous bytes) write linearly.
 template <int D, bool V_F8>
 struct PfGeo {
   static constexpr int K_CH = D / 16;                  // chunks per K row (codes)
