@@ -77,9 +77,13 @@ constexpr int PF_RSRC_W3 = 0x00020000;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // LDS tile geometry.  Rows are unpadded; the 16-byte chunk c of row r sits at
-// chunk position c ^ swizzle(r), which spreads the rows of one chunk column
-// over the banks (unswizzled rows read at half the rate), while the direct
-// loads (64 lanes x 16 contiguous bytes) write linearly.
+// chunk position c ^ swizzle(r), while the direct loads (64 lanes x 16
+// contiguous bytes) write linearly.  On this LDS (measured) a 16-byte read
+// is served in four passes of 16 lanes -- each half-wave split by the parity
+// of lane bits 2..4 -- across 64 four-byte banks, and a 16-byte write in
+// eight passes of 8 consecutive lanes across 32 banks.  The swizzles give the
+// 16 lanes of every K and V^T read pass 16 distinct 16-byte bank groups, and
+// the two rows of every 8-lane pass of the fp8 V^T stores opposite halves.
 template <int D, bool V_F8>
 struct PfGeo {
   static constexpr int K_CH = D / 16;                  // chunks per K row (codes)
@@ -97,8 +101,8 @@ struct PfGeo {
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = NST * KBYTES;
   static constexpr int LDS = V_OFF + NV_ST * VBYTES;
-  static ATTNQ_DEV int ksw(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
-  static ATTNQ_DEV int vsw(int r) { return (r >> 1) & 7; }
+  static ATTNQ_DEV int ksw(int r) { return D == 128 ? (((r >> 1) & 1) | (((r >> 2) & 1) << 2)) : (((r >> 2) & 1) << 1); }
+  static ATTNQ_DEV int vsw(int r) { return r & 7; }
   // token-major fp16 V rows (paged form): D / 8 chunks per row
   static ATTNQ_DEV int tsw(int r) { return r & (D / 8 - 1); }
 };
