@@ -54,7 +54,7 @@ constexpr int MLA_NOPE = 512, MLA_ROPE = 64, MLA_ROW = 656;
 constexpr int MLA_CPR = MLA_ROW / 16;            // 41 16-byte chunks per row
 constexpr int MLA_RAW = (MLA_STEP * MLA_CPR + MLA_THREADS - 1) / MLA_THREADS;  // 2
 constexpr int NAT_ROW = MLA_NOPE + 16;           // bf16 per token row: 1056 B, 8 banks apart
-constexpr int ROPE_ROW = MLA_ROPE + 8;           // bf16 per rope row
+constexpr int ROPE_ROW = MLA_ROPE + 16;          // bf16 per rope row: 160 B
 constexpr int MLA_SPLIT_TOKENS = 512;            // indices per split (16 steps)
 constexpr int MLA_BT_LDS = 2048;                 // block-table rows up to this long are read into LDS
 static_assert(MLA_THREADS >= MLA_SPLIT_TOKENS, "one slot per thread");
@@ -65,7 +65,7 @@ constexpr float MLA_TILE_SUM_MAX = 16384.0f;
 
 struct MlaStage {
   uint16_t nat[MLA_STEP * NAT_ROW + 8];  // bf16 codes, row r at nat_row(r)
-  uint16_t rope[MLA_STEP * ROPE_ROW];
+  uint16_t rope[MLA_STEP * ROPE_ROW + 8];  // row r at rope_row(r)
   float scale[4][MLA_STEP];          // [tile][token]
 };
 constexpr int MLA_NBUF = 2;  // staging buffers: step st computes, step st + 1 is staged
@@ -80,18 +80,30 @@ struct MlaLds {
   int bt[MLA_BT_LDS];             // the sequence's block-table row, when it fits
 };
 
-// LDS serves reads 32 lanes per pass (16-byte) or 64 lanes per pass
-// (8-byte) across 128 4-byte banks, and 16-byte writes 16 lanes per pass
-// across 64 banks.  Rows of staged codes are 264 banks apart and rows 16..31
-// sit 4 banks further on, so the 16 rows x 2 channel groups of a K-operand
-// read and the 16 rows x 32 bytes of a transposed read each hit distinct
-// banks.
+// LDS passes (measured): a 16-byte read is served in four passes of 16
+// lanes -- each half-wave split by the parity of lane bits 2..4 -- across 64
+// four-byte banks, an 8-byte read (plain or transposed) in two passes of 32
+// lanes across 64 banks, a 16-byte write in eight passes of 8 consecutive
+// lanes across 32 banks and an 8-byte write in four passes of 16 lanes
+// across 32 banks.  Every access below keeps each pass on distinct banks.
+//
+// Staged code rows are 1056 bytes (66 16-byte groups) apart and rows 16..31
+// sit 16 bytes further on: the K-operand reads (16 rows x 2 adjacent 16-byte
+// groups per pass) and the transposed reads (8 rows x 32 bytes per pass)
+// spread over all banks, and a staging write pass covers rows 4a..4a+3 and
+// 16+4a..16+4a+3 (stage_row), which land on 8 distinct 16-byte groups.
 ATTNQ_DEV int nat_row(int r) { return r * NAT_ROW + 8 * (r >> 4); }
+// Rope rows: 160 bytes (10 groups: twice an odd number, so 16 rows of a read
+// pass fall on 8 distinct even groups per lane parity), rows 16..31 16 bytes on.
+ATTNQ_DEV int rope_row(int r) { return r * ROPE_ROW + 8 * (r >> 4); }
+// Token row of staging chunk c (c % 32 -> a permutation of the step's rows).
+ATTNQ_DEV int stage_row(int c) { return (((c >> 2) & 1) << 4) | (((c >> 3) & 3) << 2) | (c & 3); }
 // Offset of (head h, token k) in a 16-head x 32-token exchange array: rows of
-// 32 floats whose 4-token groups are XOR-swizzled by h / 2, so the 16-byte
-// writes and reads of 16 heads x one token group and the 8-byte reads and
-// writes of 4 heads x 32 tokens each hit distinct banks.
-ATTNQ_DEV int xsw(int h, int k) { return h * MLA_STEP + ((((k >> 2) ^ ((h >> 1) & 7)) << 2) | (k & 3)); }
+// 32 floats whose 4-token groups are XOR-swizzled by h % 8, so the 16-byte
+// writes of 8 heads x one token group, the 16-byte reads of 16 heads x two
+// token groups and the 8-byte reads and writes of heads x 32 tokens each hit
+// distinct banks.
+ATTNQ_DEV int xsw(int h, int k) { return h * MLA_STEP + ((((k >> 2) ^ (h & 7)) << 2) | (k & 3)); }
 
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) lds_h4* lds_h4_ptr;
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
   // step's p are inf/NaN and force the exact path
   float m_ref = -INFINITY, l_run = 0.f;
 
-  // ---- staging: chunk c of a step = (row c % 32, 16-byte column c / 32).
+  // ---- staging: chunk c of a step = (row stage_row(c), 16-byte column c / 32).
   // The rows of step st + 1 are gathered into registers while step st computes.
   u32x4 raw[MLA_RAW];
   auto gather = [&](int st) {
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
     static_for<0, MLA_RAW>([&](auto ki) {
       constexpr int k = decltype(ki)::value;
       const int c = threadIdx.x + k * MLA_THREADS;
-      rr[k] = c < MLA_STEP * MLA_CPR ? L.row_idx[st * MLA_STEP + (c % MLA_STEP)] : -1;
+      rr[k] = c < MLA_STEP * MLA_CPR ? L.row_idx[st * MLA_STEP + stage_row(c)] : -1;
     });
     static_for<0, MLA_RAW>([&](auto ki) {
       constexpr int k = decltype(ki)::value;
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
       constexpr int k = decltype(ki)::value;
       const int c = threadIdx.x + k * MLA_THREADS;
       if (c < MLA_STEP * MLA_CPR) {
-        const int r = c % MLA_STEP, col = (c / MLA_STEP) * 16;
+        const int r = stage_row(c), col = (c / MLA_STEP) * 16;
         if (col < MLA_NOPE) {
           uint32_t h[8];
 #pragma unroll
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
           dn[0] = u32x4{h[0], h[1], h[2], h[3]};
           dn[1] = u32x4{h[4], h[5], h[6], h[7]};
         } else if (col < MLA_NOPE + 2 * MLA_ROPE) {
-          *reinterpret_cast<u32x4*>(&B.rope[r * ROPE_ROW + (col - MLA_NOPE) / 2]) = raw[k];
+          *reinterpret_cast<u32x4*>(&B.rope[rope_row(r) + (col - MLA_NOPE) / 2]) = raw[k];
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) B.scale[u][r] = __uint_as_float(raw[k][u]);  // zero for unused rows
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void k_mla_split(const MlaArgs a, c
           v4f racc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const v8bf kop = *reinterpret_cast<const v8bf*>(&B.rope[(16 * j + n) * ROPE_ROW + 8 * g + 32 * m]);
+            const v8bf kop = *reinterpret_cast<const v8bf*>(&B.rope[rope_row(16 * j + n) + 8 * g + 32 * m]);
             racc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[m], racc, 0, 0, 0);
           }
           sp += racc;
