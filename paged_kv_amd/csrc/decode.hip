@@ -177,16 +177,23 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
   float m_ref = -INFINITY, l_run = 0.f;
   const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
 
-  // one step on K registers kc while step st+1 is fetched into kn.  The
-  // fetch is unconditional (the last step re-reads its own, cached, rows) so
-  // that every step issues the same eight loads and the wait counts below are
-  // exact.
-  auto step = [&](auto stage_c, int st, const KRegs& kc, KRegs& kn) {
+  // one step on K registers kc while step st+1 is fetched into kn.  In the
+  // loop the fetch is unconditional (the last step of an even count re-reads
+  // its own, cached, rows into registers the code after the loop may read),
+  // so every loop step issues the same 2*KH + NVL loads and the wait below is
+  // exact.  The step after the loop (LAST, odd counts) fetches nothing and
+  // waits for every load: a K prefetch there would be dead, the compiler drops
+  // dead loads, and a count that assumed them would let the previous step's
+  // V loads into the stage it reads still be in flight.
+  auto step = [&](auto stage_c, auto last_c, int st, const KRegs& kc, KRegs& kn) {
     constexpr int STAGE = decltype(stage_c)::value;  // == st % 2
+    constexpr bool LAST = decltype(last_c)::value;
     const bool more = st + 1 < nsteps;
-    const int nx = more ? st + 1 : st;
-    load_k(nx, kn);
-    load_v(nx, STAGE ^ 1);
+    if constexpr (!LAST) {
+      const int nx = more ? st + 1 : st;
+      load_k(nx, kn);
+      load_v(nx, STAGE ^ 1);
+    }
     // ---- S^T = K Q^T for the two 16-token blocks
     float s[2][4];
 #pragma unroll
@@ -240,7 +247,8 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
       }
     // ---- O^T += V^T P^T; the step's V stage has landed (only step st+1's
     // KH*2 K loads and NVL V loads may still be in flight)
-    dec_wait_vm<2 * KH + NVL>();
+    if constexpr (LAST) dec_wait_vm<0>();
+    else dec_wait_vm<2 * KH + NVL>();
     // the transposed reads as one block (the compiler would otherwise drain
     // every in-flight direct load before each of them)
     v2i raw[D / 16];
@@ -290,10 +298,10 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void k_decode_split(const DecodeArg
   // still in flight at the top of the loop and wait for it there)
   int st = 0;
   for (; st + 1 < nsteps; st += 2) {
-    step(std::integral_constant<int, 0>{}, st, ka, kb);
-    step(std::integral_constant<int, 1>{}, st + 1, kb, ka);
+    step(std::integral_constant<int, 0>{}, std::false_type{}, st, ka, kb);
+    step(std::integral_constant<int, 1>{}, std::false_type{}, st + 1, kb, ka);
   }
-  if (st < nsteps) step(std::integral_constant<int, 0>{}, st, ka, kb);
+  if (st < nsteps) step(std::integral_constant<int, 0>{}, std::true_type{}, st, ka, kb);
   dec_wait_vm<0>();  // no direct load may outlive the workgroup's LDS
   // ---- partial results: O_c = O / l (times the V descale, fp8 -> fp16 was exact),
   //      lse_c = m + log2(l) in log2 units

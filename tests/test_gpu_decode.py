@@ -40,6 +40,22 @@ def test_decode_small(ps):
     _check(x, 1 / math.sqrt(128), label=f"ps={ps}")
 
 
+def test_decode_odd_step_tails_repeated():
+    """Chunks with an odd number of 32-token steps end in a step that fetches
+    nothing ahead: its V stage, loaded during the step before, must have
+    landed before its transposed reads.  Tails of 1, 3, .. 15 steps, each call
+    against the oracle once, then bit-identical over repeated calls (the split
+    and merge are deterministic)."""
+    lens = [512 + 32 * (2 * i + 1) - 7 for i in range(8)] + [32 * (2 * i + 1) for i in range(8)]
+    x = gen.paged_decode_inputs(77, lens, 32, 8, 128, page_size=16)
+    p, _ = _check(x, 1 / math.sqrt(128), label="odd step tails")
+    first = p.o.clone()
+    for _ in range(20):
+        p.run()
+        torch.cuda.synchronize()
+        assert torch.equal(p.o, first)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 1), (12, 4), (6, 3), (10, 5), (16, 16)])
 def test_decode_group_sizes(hq, hkv):
     x = gen.paged_decode_inputs(52, [700, 64, 2000], hq, hkv, 128, page_size=16)
