@@ -103,8 +103,10 @@ struct PfGeo {
   static constexpr int LDS = V_OFF + NV_ST * VBYTES;
   static ATTNQ_DEV int ksw(int r) { return D == 128 ? (((r >> 1) & 1) | (((r >> 2) & 1) << 2)) : (((r >> 2) & 1) << 1); }
   static ATTNQ_DEV int vsw(int r) { return r & 7; }
-  // token-major fp16 V rows (paged form): D / 8 chunks per row
-  static ATTNQ_DEV int tsw(int r) { return r & (D / 8 - 1); }
+  // token-major fp16 V rows (paged form): D / 8 chunks per row.  Even
+  // swizzles: a transposed-read pass (8 rows x 2 chunks of each) covers all
+  // 16 (D = 128) or, per row parity, all 8 (D = 64) chunk positions.
+  static ATTNQ_DEV int tsw(int r) { return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1; }
 };
 
 ATTNQ_DEV __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, uint32_t bytes) {
@@ -429,11 +431,13 @@ __global__ __launch_bounds__(PfShape<D>::THREADS, V_F8 ? 2 : 3) void k_prefill(c
       pf_widen_fp8(vreg[c], lo, hi);
       if constexpr (PAGED) {
         // token-major fp16 rows of D * 2 bytes, 16-byte chunk j of row r at
-        // chunk position j ^ (r % chunks per row)
+        // chunk position j ^ tsw(r).  Half of each 8-lane write pass stores
+        // its odd chunk first, so every pass covers 8 distinct positions.
         const int r = idx / (D / 16), cc = idx % (D / 16);
         uint8_t* row = smem + G::V_OFF + stage * G::VBYTES + r * (2 * D);
-        *reinterpret_cast<u32x4*>(row + ((2 * cc) ^ G::tsw(r)) * 16) = lo;
-        *reinterpret_cast<u32x4*>(row + ((2 * cc + 1) ^ G::tsw(r)) * 16) = hi;
+        const int sw = D == 128 ? (cc >> 2) & 1 : r & 1;
+        *reinterpret_cast<u32x4*>(row + ((2 * cc + sw) ^ G::tsw(r)) * 16) = sw ? hi : lo;
+        *reinterpret_cast<u32x4*>(row + ((2 * cc + 1 - sw) ^ G::tsw(r)) * 16) = sw ? lo : hi;
       } else {
         const int r = idx >> 2, j = idx & 3;
         uint8_t* row = smem + G::V_OFF + stage * G::VBYTES + r * 128;
