@@ -42,14 +42,15 @@ constexpr float DEC_REF_SLACK = 8.0f;             // log2 headroom before a resc
 
 // 16-byte chunk position of chunk c in V tile row t is c ^ dec_vsw<D>(t), so
 // that the rows the transposed reads of one LDS pass name land in distinct
-// bank groups.  D = 128 (8 chunks per row): the 8 rows one 16-lane group
-// reads fall in 8 distinct (row parity, chunk) groups.  D = 64 (4 chunks,
-// rows 16 banks apart): the 16 rows two 16-lane groups read, 4g + r and
-// 16 + 4g + r for g in {0, 1} or {2, 3}, take the 4 row offsets times the 4
-// chunk positions.
+// bank groups.  An 8-byte (transposed) read is served in two passes of 32
+// lanes across 64 four-byte banks (measured); the 32 lanes of a pass name 16
+// rows (4g + r and 16 + 4g + r, r < 4, g in {0, 1} or {2, 3}) x 8 bytes of
+// one chunk column.  D = 128 (rows 32 banks apart): the 8 rows of each row
+// parity take the 8 chunk positions.  D = 64 (rows 16 banks apart): the 4
+// rows of each row offset take the 4 chunk positions.
 template <int D>
 ATTNQ_DEV int dec_vsw(int t) {
-  if constexpr (D == 128) return ((t >> 1) + 2 * (t >> 4)) & 7;
+  if constexpr (D == 128) return ((t >> 1) & 1) | (((t >> 2) & 1) << 1) | (((t >> 4) & 1) << 2);
   else return ((t >> 2) & 1) | (((t >> 4) & 1) << 1);
 }
 
